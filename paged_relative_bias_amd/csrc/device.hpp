@@ -1,0 +1,67 @@
+// Device helpers for the gfx950 (CDNA4) kernels: vector types, bf16
+// conversion, MFMA wrappers and wave-level exchanges.  Wave64 only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ira {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // RNE
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+
+// 2^x on the transcendental unit; callers only pass x <= 0 or -inf.
+__device__ __forceinline__ float fast_exp2(float x) {
+  return __builtin_amdgcn_exp2f(x);
+}
+
+// Value held by lane (lane ^ mask) of the same wave.
+__device__ __forceinline__ float xor_lane(float x, int mask) {
+  return __shfl_xor(x, mask, 64);
+}
+
+// --- MFMA wrappers (accumulate in fp32) -----------------------------------
+// 32x32 output tile: lane l holds column l % 32, rows 8*(i/4) + 4*(l/32) + i%4
+// for i = 0..15.  16x16 output tile: lane l holds column l % 16, rows
+// 4*(l/16) + i for i = 0..3.  For the operands, both A and B are indexed by
+// (lane group, element) -> k with the same rule, so a consistent assignment
+// of contraction indices to (lane group, element) on both sides is all that
+// correctness needs.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
+__device__ __forceinline__ int imax(int a, int b) { return a > b ? a : b; }
+__device__ __forceinline__ int iclamp(int x, int lo, int hi) {
+  return imin(imax(x, lo), hi);
+}
+// Largest multiple of m (a power of two) not above x, for any sign of x.
+__device__ __forceinline__ int floor_to(int x, int m) { return x & ~(m - 1); }
+
+}  // namespace ira

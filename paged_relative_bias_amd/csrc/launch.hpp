@@ -1,0 +1,66 @@
+// Kernel parameter blocks and launchers shared by the host ABI (abi.cpp) and
+// the kernel translation units.  Internal to the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ira {
+
+// Keys per prefill key tile and per decode wave tile.
+constexpr int kPrefillKeys = 64;
+constexpr int kDecodeKeys = 32;
+constexpr int kDecodeWaves = 4;
+constexpr int kMaxSplits = 128;
+constexpr int kMaxGroup = 16;
+
+struct PrefillParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const int32_t* cu_q_lens;
+  const void* rel;
+  void* out;
+  int32_t hq, hkv, group;
+  int32_t num_blocks, max_blocks, rel_len, window, total_q;
+  int32_t bq;         // query tokens per workgroup
+  int32_t sb;         // bias entries staged per row and key tile
+  int32_t sb_pitch;   // bytes between staged bias rows
+  float scale;
+};
+
+struct DecodeParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const void* rel;
+  void* out;          // final output (num_splits == 1)
+  float* part_o;      // [splits, B, Hq, D] normalised partial outputs
+  float* part_lse;    // [splits, B, Hq]
+  int32_t num_seqs, hq, hkv, group;
+  int32_t num_blocks, max_blocks, rel_len, window, num_splits;
+  float scale;
+};
+
+struct CombineParams {
+  const float* part_o;
+  const float* part_lse;
+  void* out;
+  int32_t rows;       // B * Hq
+  int32_t num_splits;
+};
+
+// dtype: 0 = bf16, 1 = fp32.  Return the launch's hipError_t.
+hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim,
+                          int num_seqs, int max_q_len, hipStream_t stream);
+size_t prefill_lds_bytes(int dtype, int head_dim, int waves, int sb_pitch);
+hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim,
+                         hipStream_t stream);
+hipError_t launch_combine(const CombineParams& p, int dtype, int head_dim,
+                          hipStream_t stream);
+
+}  // namespace ira

@@ -1,0 +1,86 @@
+"""Helpers for the GPU parity tests: move a batch to the device, call the
+library through its C ABI binding, compare with the oracle."""
+import numpy as np
+import torch
+
+import oracle
+from paged_relative_bias_amd import binding
+
+# Tolerances.  bf16: the stated bar, max-abs 1e-2 and mean-abs 1e-3 against
+# the unrounded fp64 oracle.  fp32: every step is fp32 (fp32 MFMA, fp32 P),
+# so errors are ~1e-6; 1e-4 leaves two orders of margin.
+TOL = {"bf16": (1e-2, 1e-3), "fp32": (1e-4, 1e-5)}
+
+
+class Dev:
+    """Device copies of a batch's tensors."""
+
+    def __init__(self, batch, device="cuda"):
+        self.batch = batch
+        self.q = batch.q.to(device)
+        self.k = batch.k_cache.to(device)
+        self.v = batch.v_cache.to(device)
+        self.rel = batch.rel_logits.to(device)
+        self.bt = torch.from_numpy(batch.block_table).to(device)
+        self.sl = torch.from_numpy(batch.seq_lens).to(device)
+        self.cu = torch.from_numpy(batch.cu_q_lens).to(device)
+
+
+def prefill(dev: Dev, out=None, stream=None):
+    b = dev.batch
+    if out is None:
+        out = torch.full_like(dev.q, float("nan"))
+    binding.prefill(dev.q, dev.k, dev.v, dev.bt, dev.sl, dev.cu, dev.rel,
+                    b.window, b.scale, out, max_q_len=b.max_q_len,
+                    max_seq_len=b.max_seq_len, stream=stream)
+    return out
+
+
+def decode(dev: Dev, splits=0, out=None, workspace=None, stream=None):
+    b = dev.batch
+    if out is None:
+        out = torch.full_like(dev.q, float("nan"))
+    binding.decode(dev.q, dev.k, dev.v, dev.bt, dev.sl, dev.rel, b.window,
+                   b.scale, out, max_seq_len=b.max_seq_len, num_splits=splits,
+                   workspace=workspace, stream=stream)
+    return out
+
+
+def compare(got: torch.Tensor, ref: np.ndarray, dtype: str, what: str = "",
+            rows=None):
+    """Element-wise check against the oracle; returns (max_abs, mean_abs)."""
+    g = got.detach().float().cpu().numpy().astype(np.float64)
+    if rows is not None:
+        g = g.reshape(-1, g.shape[-1])[rows]
+    ref = ref.reshape(g.shape)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    err = np.abs(g - ref)
+    mx, mean = float(err.max()), float(err.mean())
+    tol_max, tol_mean = TOL[dtype]
+    print(f"  {what}: max_abs={mx:.3e} mean_abs={mean:.3e}", flush=True)
+    assert mx <= tol_max and mean <= tol_mean, (
+        f"{what}: max_abs {mx:.3e} (tol {tol_max}) mean_abs {mean:.3e} "
+        f"(tol {tol_mean}); worst at {np.unravel_index(err.argmax(), err.shape)}")
+    return mx, mean
+
+
+def sample_rows(batch, n_random: int, seed: int = 0, first_positions: int = 3):
+    """Flat (row * Hq + h) indices: a seeded random subset plus every head of
+    the first `first_positions` positions of each sequence (where few keys
+    make bf16 rounding matter most)."""
+    rng = np.random.default_rng(seed)
+    Hq = batch.num_q_heads
+    total = batch.total_q * Hq
+    pick = set(rng.choice(total, size=min(n_random, total), replace=False).tolist())
+    for s in range(batch.num_seqs):
+        n, L = int(batch.q_lens[s]), int(batch.seq_lens[s])
+        for t in range(n):
+            if L - n + t < first_positions:
+                r = int(batch.cu_q_lens[s]) + t
+                pick.update(range(r * Hq, (r + 1) * Hq))
+    return np.array(sorted(pick), dtype=np.int64)
+
+
+def oracle_rows(batch, rows, threads=0):
+    out, _ = oracle.run_batch(batch, rows=rows, threads=threads)
+    return out

@@ -1,0 +1,227 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Every input is seeded and synthetic (paged_relative_bias_amd.inputs) with
+NaN in every byte the kernels must never read.  Bar: bf16 outputs within
+max-abs 1e-2 and mean-abs 1e-3 of the unrounded oracle; fp32 within 1e-4 /
+1e-5; index and mask work bit-exact (page permutation, determinism).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_relative_bias_amd import binding, inputs
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    st, msg = binding.check_device(0)
+    assert st == binding.OK, msg
+    yield
+    torch.cuda.synchronize()
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _mk(seed, L, n, *, Hq=48, Hkv=16, D=128, W=512, R=None, dtype="bf16",
+        max_blocks=None, spare=64):
+    rng = np.random.default_rng(seed)
+    if R is None:
+        R = W if W > 0 else 8192
+    return inputs.make_batch(rng, L, n, num_q_heads=Hq, num_kv_heads=Hkv,
+                             head_dim=D, window=W, rel_len=R, dtype=dtype,
+                             max_blocks_per_seq=max_blocks, spare_pages=spare)
+
+
+# ---------------------------------------------------------------- prefill --
+
+def test_tiny_prefill_fp32_full():
+    b = inputs.tiny()
+    _say("tiny prefill fp32", b.seq_lens.tolist())
+    out = U.prefill(U.Dev(b))
+    ref, _ = oracle.run_batch(b)
+    U.compare(out, ref, "fp32", "tiny")
+
+
+PREFILL_CASES = [
+    # (name, seed, L, n, Hq, Hkv, D, W, R, dtype)
+    ("local_ragged", 1, [700, 333, 97], [700, 333, 97], 48, 16, 128, 512, 512, "bf16"),
+    ("local_chunked", 2, [900, 1200], [130, 1], 48, 16, 128, 512, 512, "bf16"),
+    ("global_ragged", 3, [640, 257, 64], [640, 100, 64], 48, 8, 128, 0, 8192, "bf16"),
+    ("global_mixed_small", 4, [1500, 77, 800, 1], [1, 77, 300, 1], 48, 8, 128, 0, 8192, "bf16"),
+    ("window_1", 5, [200, 37], [200, 37], 12, 4, 128, 1, 8, "bf16"),
+    ("window_63", 6, [300], [300], 12, 4, 128, 63, 64, "bf16"),
+    ("clamp_active", 7, [400, 150], [400, 50], 12, 4, 128, 0, 40, "bf16"),
+    ("head_dim_64", 8, [333, 64], [333, 64], 8, 2, 64, 100, 104, "bf16"),
+    ("mha_g1", 9, [250], [250], 4, 4, 128, 64, 64, "bf16"),
+    ("g8_bq32", 10, [300, 45], [300, 45], 64, 8, 128, 0, 512, "bf16"),
+    ("g16_bq16", 11, [170], [170], 32, 2, 128, 48, 48, "bf16"),
+    ("fp32_d128", 12, [150, 20], [150, 20], 8, 4, 128, 40, 40, "fp32"),
+    ("zero_len_seq", 13, [300, 5, 90], [300, 0, 90], 12, 4, 128, 64, 64, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=[c[0] for c in PREFILL_CASES])
+def test_prefill_matches_oracle(case):
+    name, seed, L, n, Hq, Hkv, D, W, R, dtype = case
+    b = _mk(seed, L, n, Hq=Hq, Hkv=Hkv, D=D, W=W, R=R, dtype=dtype)
+    _say(f"prefill {name}: L={L} n={n} Hq={Hq} Hkv={Hkv} D={D} W={W} R={R} {dtype}")
+    out = U.prefill(U.Dev(b))
+    ref, _ = oracle.run_batch(b)
+    U.compare(out, ref, dtype, name)
+
+
+def test_prefill_deterministic_and_page_permutation_bitexact():
+    b = _mk(20, [600, 211], [600, 211], Hq=12, Hkv=4, W=128, R=128)
+    _say("prefill determinism / page permutation")
+    d = U.Dev(b)
+    o1 = U.prefill(d)
+    o2 = U.prefill(d)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    # Same logical cache, different physical pages.
+    perm = np.random.default_rng(5).permutation(b.num_blocks)
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(len(perm))
+    k2 = torch.empty_like(b.k_cache)
+    v2 = torch.empty_like(b.v_cache)
+    k2[torch.from_numpy(inv)] = b.k_cache
+    v2[torch.from_numpy(inv)] = b.v_cache
+    bt2 = np.where(b.block_table >= 0, inv[np.maximum(b.block_table, 0)], -1).astype(np.int32)
+    b2 = dataclasses.replace(b, k_cache=k2, v_cache=v2, block_table=bt2)
+    o3 = U.prefill(U.Dev(b2))
+    assert torch.equal(o1.view(torch.int16), o3.view(torch.int16))
+
+
+def test_prefill_chunked_equals_whole():
+    """Two chunked calls (first k tokens, then the rest on top) give the same
+    rows as one call.  Key tiles start at key 0 in both (full causal), and a
+    tile that is fully masked for a column leaves its state bit-unchanged
+    (rescale by exactly 1, add exactly 0), so the rows are bit-equal."""
+    b = _mk(21, [520], [520], Hq=12, Hkv=4, W=0, R=1024)
+    _say("prefill chunked vs whole")
+    whole = U.prefill(U.Dev(b))
+    k = 200
+    c1 = dataclasses.replace(b, seq_lens=np.array([520 - 320], np.int32),
+                             q_lens=np.array([k], np.int32),
+                             cu_q_lens=np.array([0, k], np.int32),
+                             q=b.q[:k].contiguous(), rel_logits=b.rel_logits[:k].contiguous())
+    c2 = dataclasses.replace(b, q_lens=np.array([320], np.int32),
+                             cu_q_lens=np.array([0, 320], np.int32),
+                             q=b.q[k:].contiguous(), rel_logits=b.rel_logits[k:].contiguous())
+    o1 = U.prefill(U.Dev(c1))
+    o2 = U.prefill(U.Dev(c2))
+    got = torch.cat([o1, o2])
+    # Same visible sets and the same per-row arithmetic order: bit-equal.
+    assert torch.equal(got.view(torch.int16), whole.view(torch.int16))
+
+
+# ----------------------------------------------------------------- decode --
+
+DECODE_CASES = [
+    # (name, seed, L, Hq, Hkv, D, W, R, splits)
+    ("local_pages", 30, [1, 15, 16, 17, 512, 513, 1000, 2049], 48, 16, 128, 512, 512, [1, 2, 4, 0]),
+    ("global_pages", 31, [1, 16, 17, 512, 513, 4095, 4096, 6000], 48, 8, 128, 0, 8192, [1, 8, 32, 0]),
+    ("global_many_splits", 32, [33, 300, 8192], 48, 8, 128, 0, 8192, [128, 37]),
+    ("clamp_active", 33, [900, 60], 12, 4, 128, 0, 64, [1, 3]),
+    ("head_dim_64", 34, [100, 300], 8, 2, 64, 200, 200, [1, 4]),
+    ("mha_g1", 35, [700], 4, 4, 128, 0, 1024, [1, 5]),
+    ("g16", 36, [450, 33], 32, 2, 128, 0, 512, [1, 6]),
+    ("fp32", 37, [300, 77], 8, 4, 64, 100, 100, [1, 4]),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=[c[0] for c in DECODE_CASES])
+def test_decode_matches_oracle(case):
+    name, seed, L, Hq, Hkv, D, W, R, splits = case
+    dtype = "fp32" if name == "fp32" else "bf16"
+    b = _mk(seed, L, [1] * len(L), Hq=Hq, Hkv=Hkv, D=D, W=W, R=R, dtype=dtype)
+    ref, _ = oracle.run_batch(b)
+    d = U.Dev(b)
+    for s in splits:
+        _say(f"decode {name}: L={L} W={W} R={R} splits={s}")
+        out = U.decode(d, splits=s)
+        U.compare(out, ref, dtype, f"{name}/s{s}")
+
+
+def test_decode_equals_last_prefill_row():
+    b = _mk(40, [700, 900], [150, 64], Hq=12, Hkv=4, W=512, R=512)
+    _say("decode vs last prefill row")
+    pre = U.prefill(U.Dev(b))
+    last = torch.from_numpy((b.cu_q_lens[1:] - 1).astype(np.int64))
+    dec = dataclasses.replace(b, q_lens=np.ones(2, np.int32),
+                              cu_q_lens=np.arange(3, dtype=np.int32),
+                              q=b.q[last].contiguous(),
+                              rel_logits=b.rel_logits[last].contiguous())
+    out = U.decode(U.Dev(dec), splits=1)
+    diff = (out.float() - pre[last.cuda()].float()).abs().max().item()
+    assert diff <= 2e-2, diff   # two bf16 paths, each within 1e-2 of exact
+
+
+def test_decode_deterministic():
+    b = _mk(41, [3000, 5000], [1, 1], Hq=48, Hkv=8, W=0, R=8192)
+    d = U.Dev(b)
+    for s in (1, 8):
+        o1 = U.decode(d, splits=s)
+        o2 = U.decode(d, splits=s)
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+# ------------------------------------------------- full workload sizes ----
+
+def _full(name):
+    return inputs.WORKLOADS[name](seed=0)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 4, 0])
+@pytest.mark.timeout(400)
+def test_full_local_decode(splits):
+    b = _full("local_decode")
+    _say(f"full local_decode splits={splits}")
+    ref, _ = oracle.run_batch(b)
+    U.compare(U.decode(U.Dev(b), splits=splits), ref, "bf16", f"local_decode/s{splits}")
+
+
+@pytest.mark.parametrize("splits", [1, 8, 32, 0])
+@pytest.mark.timeout(400)
+def test_full_global_decode(splits):
+    b = _full("global_decode")
+    _say(f"full global_decode splits={splits}")
+    ref, _ = oracle.run_batch(b)
+    U.compare(U.decode(U.Dev(b), splits=splits), ref, "bf16", f"global_decode/s{splits}")
+
+
+@pytest.mark.timeout(400)
+def test_full_local_prefill_sampled():
+    b = _full("local_prefill")
+    _say("full local_prefill (sampled rows)")
+    out = U.prefill(U.Dev(b))
+    rows = U.sample_rows(b, 6000, seed=1)
+    U.compare(out, U.oracle_rows(b, rows), "bf16", "local_prefill", rows=rows)
+
+
+@pytest.mark.timeout(400)
+def test_full_global_mixed_sampled():
+    b = _full("global_mixed")
+    _say("full global_mixed as one prefill call (sampled rows)")
+    d = U.Dev(b)
+    out = U.prefill(d)
+    rows = U.sample_rows(b, 4000, seed=2)
+    ref = U.oracle_rows(b, rows)
+    U.compare(out, ref, "bf16", "global_mixed/prefill", rows=rows)
+    # The same batch as prefill(chunks) + decode(48 rows).
+    dec, pre = inputs.split_mixed(b)
+    o_pre = U.prefill(U.Dev(pre))
+    o_dec = U.decode(U.Dev(dec), splits=0)
+    ref_dec, _ = oracle.run_batch(dec)
+    U.compare(o_dec, ref_dec, "bf16", "global_mixed/decode")
+    rows_p = U.sample_rows(pre, 3000, seed=3)
+    U.compare(o_pre, U.oracle_rows(pre, rows_p), "bf16", "global_mixed/chunks", rows=rows_p)
