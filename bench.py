@@ -125,12 +125,18 @@ def cpu_baseline(batch, budget_s=20.0):
         rows = rng.choice(total_rows, size=n, replace=False)
         frac = n / total_rows
         sample = f"{n} random (row, head) pairs of {total_rows} ({100 * frac:.2f}%)"
-    t0 = time.perf_counter()
-    oracle.run_batch(batch, rows=rows)
-    dt = time.perf_counter() - t0
+    # Repeat short runs until at least ~2 s have been timed (mean per run).
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        oracle.run_batch(batch, rows=rows)
+        runs += 1
+        if time.perf_counter() - t0 >= min(2.0, budget_s):
+            break
+    dt = (time.perf_counter() - t0) / runs
     tokens = batch.total_q * frac
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads,
-            "kind": "oracle", "sample": sample, "seconds": round(dt, 3)}
+            "kind": "oracle", "sample": sample, "seconds_per_run": round(dt, 4),
+            "runs": runs}
 
 
 def main():

@@ -7,9 +7,19 @@ import oracle
 from paged_relative_bias_amd import binding
 
 # Tolerances.  bf16: the stated bar, max-abs 1e-2 and mean-abs 1e-3 against
-# the unrounded fp64 oracle.  fp32: every step is fp32 (fp32 MFMA, fp32 P),
-# so errors are ~1e-6; 1e-4 leaves two orders of margin.
+# the unrounded fp64 oracle.  Where |ref| >= 4 the spacing of bf16 values is
+# at least 1/32, so even the correctly rounded result can sit 1/64 > 1e-2
+# away; there the per-element bar is one bf16 ulp of |ref| instead (the
+# mean-abs bar still covers every element).  fp32: every step is fp32 (fp32
+# MFMA, fp32 P), so errors are ~1e-6; 1e-4 leaves two orders of margin.
 TOL = {"bf16": (1e-2, 1e-3), "fp32": (1e-4, 1e-5)}
+BF16_EXACT_BAR_LIMIT = 4.0
+
+
+def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 values at |x| (8 significant bits)."""
+    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126)))
+    return np.exp2(e - 7)
 
 
 class Dev:
@@ -57,10 +67,18 @@ def compare(got: torch.Tensor, ref: np.ndarray, dtype: str, what: str = "",
     err = np.abs(g - ref)
     mx, mean = float(err.max()), float(err.mean())
     tol_max, tol_mean = TOL[dtype]
-    print(f"  {what}: max_abs={mx:.3e} mean_abs={mean:.3e}", flush=True)
-    assert mx <= tol_max and mean <= tol_mean, (
-        f"{what}: max_abs {mx:.3e} (tol {tol_max}) mean_abs {mean:.3e} "
-        f"(tol {tol_mean}); worst at {np.unravel_index(err.argmax(), err.shape)}")
+    bar = np.full(err.shape, tol_max)
+    big = np.zeros(err.shape, dtype=bool)
+    if dtype == "bf16":
+        big = np.abs(ref) >= BF16_EXACT_BAR_LIMIT
+        bar[big] = bf16_ulp(ref[big])
+    small_mx = float(err[~big].max()) if (~big).any() else 0.0
+    print(f"  {what}: max_abs={mx:.3e} (|ref|<4: {small_mx:.3e}) mean_abs={mean:.3e} "
+          f"n={err.size} n_|ref|>=4={int(big.sum())}", flush=True)
+    worst = np.unravel_index((err - bar).argmax(), err.shape)
+    assert np.all(err <= bar) and mean <= tol_mean, (
+        f"{what}: max_abs {mx:.3e} (bar {tol_max}, one ulp where |ref|>=4) mean_abs "
+        f"{mean:.3e} (tol {tol_mean}); worst at {worst}: got {g[worst]} ref {ref[worst]}")
     return mx, mean
 
 
