@@ -68,7 +68,7 @@ typedef enum { INKLING_DTYPE_BF16 = 0, INKLING_DTYPE_FP32 = 1 } inkling_dtype_t;
 
 /* Shapes of one call.  Read during the call only, never retained. */
 typedef struct {
-  int32_t num_seqs;           /* B                                           */
+  int32_t num_seqs;           /* B (at most 65535)                           */
   int32_t num_q_heads;        /* Hq                                          */
   int32_t num_kv_heads;       /* Hkv; Hq % Hkv == 0 and Hq / Hkv <= 16        */
   int32_t head_dim;           /* 64 or 128                                   */

@@ -30,6 +30,8 @@ inkling_status_t check_dims(const inkling_rel_attn_dims_t* d) {
       d->total_q < 0 || d->max_q_len < 0 || d->max_seq_len < 0)
     return INKLING_ERR_INVALID_ARGUMENT;
   if (d->num_q_heads % d->num_kv_heads != 0) return INKLING_ERR_INVALID_ARGUMENT;
+  // Sequences and KV heads index grid dimensions limited to 65535.
+  if (d->num_seqs > 65535 || d->num_kv_heads > 65535) return INKLING_ERR_UNSUPPORTED;
   if (d->dtype != INKLING_DTYPE_BF16 && d->dtype != INKLING_DTYPE_FP32)
     return INKLING_ERR_UNSUPPORTED;
   if (d->head_dim != 64 && d->head_dim != 128) return INKLING_ERR_UNSUPPORTED;

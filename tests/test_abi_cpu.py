@@ -69,6 +69,7 @@ INVALID, UNSUP = 1, 2
     (dict(num_blocks=0), INVALID),
     (dict(max_blocks_per_seq=4), INVALID),                  # 64 keys < 8192
     (dict(max_q_len=9000), INVALID),                        # > max_seq_len
+    (dict(num_seqs=70000, total_q=70000), UNSUP),           # grid limit
 ])
 def test_bad_shapes_are_rejected_before_launch(kw, status):
     assert _prefill(_dims(**kw)) == status
