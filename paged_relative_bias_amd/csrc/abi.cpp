@@ -172,18 +172,31 @@ inkling_status_t inkling_rel_attn_prefill(const void* q, const void* k_cache, co
   p.window = window;
   p.total_q = dims->total_q;
   p.scale = scale;
-  // Query tokens per workgroup: 2 * G * bq threads, at most 768.
-  p.bq = p.group <= 6 ? 64 : (p.group <= 12 ? 32 : 16);
-  const int vec = (int)(16 / dtype_size(dims->dtype));
+  // Query tokens per workgroup: G heads x bq tokens fill the 4 waves' 128
+  // MFMA columns.
+  p.bq = 128 / p.group;
+  const int waves = kPrefillWaves;
+  const size_t esz = dtype_size(dims->dtype);
+  const int vec = (int)(16 / esz);
   p.sb = std::min(dims->rel_len, kPrefillKeys + vec);
-  int row_dw = (int)((p.sb * dtype_size(dims->dtype) + 3) / 4);
+  int row_dw = (int)((p.sb * esz + 3) / 4);
   if ((row_dw & 1) == 0) row_dw += 1;  // odd dword pitch spreads LDS banks
   p.sb_pitch = row_dw * 4;
-  const int waves = (p.group * p.bq + 31) / 32;
-  if (prefill_lds_bytes(dims->dtype, dims->head_dim, waves, p.sb_pitch) > 160 * 1024)
+  p.nqb = (dims->max_q_len + p.bq - 1) / p.bq;
+  p.num_seqs = dims->num_seqs;
+  // Pages a workgroup's key range can touch.
+  const int64_t span = window > 0 ? (int64_t)p.bq + window - 1 : (int64_t)dims->max_seq_len;
+  p.pid_cap = (int32_t)std::min<int64_t>(dims->max_blocks_per_seq, (span + 15) / 16 + 2);
+  if (prefill_lds_bytes(dims->dtype, dims->head_dim, waves, p.sb_pitch, p.pid_cap) > 160 * 1024)
     return INKLING_ERR_UNSUPPORTED;
-  const hipError_t e = launch_prefill(p, dims->dtype, dims->head_dim, dims->num_seqs,
-                                      dims->max_q_len, static_cast<hipStream_t>(stream));
+  // 32-bit buffer offsets: one page, and the bias rows of one query block.
+  if ((int64_t)16 * dims->num_kv_heads * dims->head_dim * (int64_t)esz >= (1LL << 31) ||
+      (int64_t)p.bq * dims->num_q_heads * dims->rel_len * (int64_t)esz >= (1LL << 31))
+    return INKLING_ERR_UNSUPPORTED;
+  if ((int64_t)p.nqb * dims->num_seqs * dims->num_kv_heads >= (1LL << 31))
+    return INKLING_ERR_UNSUPPORTED;
+  const hipError_t e = launch_prefill(p, dims->dtype, dims->head_dim,
+                                      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? INKLING_OK : INKLING_ERR_LAUNCH;
 }
 

@@ -8,7 +8,10 @@
 namespace ira {
 
 // Keys per prefill key tile and per decode wave tile.
-constexpr int kPrefillKeys = 64;
+constexpr int kPrefillKeys = 32;
+// Prefill workgroups have 4 waves: 128 MFMA columns = G heads x
+// floor(128 / G) query tokens.
+constexpr int kPrefillWaves = 4;
 constexpr int kDecodeKeys = 32;
 constexpr int kDecodeWaves = 4;
 constexpr int kMaxSplits = 128;
@@ -28,6 +31,9 @@ struct PrefillParams {
   int32_t bq;         // query tokens per workgroup
   int32_t sb;         // bias entries staged per row and key tile
   int32_t sb_pitch;   // bytes between staged bias rows
+  int32_t nqb;        // query blocks per sequence (ceil(max_q_len / bq))
+  int32_t num_seqs;
+  int32_t pid_cap;    // entries of the per-workgroup page-id table
   float scale;
 };
 
@@ -55,9 +61,8 @@ struct CombineParams {
 };
 
 // dtype: 0 = bf16, 1 = fp32.  Return the launch's hipError_t.
-hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim,
-                          int num_seqs, int max_q_len, hipStream_t stream);
-size_t prefill_lds_bytes(int dtype, int head_dim, int waves, int sb_pitch);
+hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim, hipStream_t stream);
+size_t prefill_lds_bytes(int dtype, int head_dim, int waves, int sb_pitch, int pid_cap);
 hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim,
                          hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, int dtype, int head_dim,

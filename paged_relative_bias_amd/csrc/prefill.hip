@@ -7,21 +7,35 @@
 // (section "Implementation") is the prior art; this is a gfx950 design.
 //
 // Work decomposition.  One workgroup per (block of `bq` query tokens,
-// sequence b, KV head g).  Its MFMA columns are the (query head in group,
-// token) pairs, head-major: column c holds head g*G + c / bq and token
-// t0 + c % bq.  Each wave owns 32 columns.  Key tiles of 64 keys sweep the
-// union of the block's visible ranges; K/V rows are gathered through the
-// block table into LDS (V transposed on the way in) and shared by all waves.
+// sequence b, KV head g); the 1-D grid is remapped so that each of the 8
+// XCDs receives a contiguous run of work, i.e. consecutive query blocks of
+// one (b, g), whose key ranges overlap, share that XCD's L2.  The MFMA
+// columns of a workgroup are its (query head in group, token) pairs,
+// head-major (column c: head g*G + c / bq, token t0 + c % bq); each wave
+// owns 32 columns.
 //
-// Per wave and 32-key half tile:
+// Key tiles of 32 keys sweep the union of the block's visible ranges,
+// double-buffered in LDS:
+//   * K rows (row-major, 16-byte pad) and V rows (row-major, 32-byte pad)
+//     are gathered through the block table by buffer loads whose 64 lanes
+//     cover keys of one page (page id uniform per instruction); the page
+//     ids of the block's range sit in an LDS table;
+//   * every wave copies the bias runs of its 32 rows for the tile: for
+//     (token, head) the tile needs one contiguous run of the distance axis,
+//     taken from an aligned window of sb entries with 16-byte loads;
+//   * the next tile's loads are issued into registers before the current
+//     tile is computed and written to the other LDS stage afterwards; the
+//     barriers order LDS only, so the loads stay in flight across them.
+// Per wave and tile:
 //   S^T[key][col] = K . Q^T       32x32x16 bf16 MFMA (32x32x2 f32 for fp32)
-//   x = scale * S + bias | -inf   bias row staged in LDS, masked by select
-//   online softmax per column     two lanes per column (l, l ^ 32)
-//   O^T[d][col] += V^T . P^T      P stays in registers as the B operand
-// The column max/sum are exchanged with the partner lane only.  The bias
-// for (token, head) over one key tile is a contiguous run of the
-// distance axis; each wave copies the runs of its 32 rows with 16-byte
-// loads, so every bias entry is read from memory about once.
+//   x = scale * S + bias          mask by select only on boundary tiles
+//   online softmax per column     two lanes per column (l, l ^ 32); the
+//                                 reference max moves only when the tile
+//                                 max exceeds it by more than 2^8 in the
+//                                 exponent, so rescaling is rare
+//   O^T[d][col] += V^T . P^T      V^T operand from ds_read_tr16_b64, P^T
+//                                 from registers; row sums of the rounded P
+//                                 with v_dot2_f32_bf16.
 #include <type_traits>
 
 #include "device.hpp"
@@ -30,68 +44,86 @@
 namespace ira {
 namespace {
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Lazy rescaling threshold, in log2 units: P may reach 2^kLazy.
+constexpr float kLazy = 8.f;
+constexpr float kLn2 = 0.6931471805599453f;
+
 template <typename T, int D>
 struct Prefill {
   static constexpr bool kBF16 = sizeof(T) == 2;
-  static constexpr int N = kPrefillKeys;              // keys per tile
-  static constexpr int VEC = 16 / sizeof(T);          // elements per 16 B
-  static constexpr int KP = D + VEC;                  // K row pitch (elements)
-  static constexpr int VP = N + (kBF16 ? 4 : 1);      // V^T row pitch
-  static constexpr int QSTEPS = kBF16 ? D / 16 : D / 2;
+  static constexpr int N = kPrefillKeys;                 // keys per tile
+  static constexpr int VEC = 16 / (int)sizeof(T);        // elements per 16 B
+  static constexpr int CPR = D / VEC;                    // chunks per K/V row
+  static constexpr int KP = D + VEC;                     // K row pitch
+  static constexpr int VP = kBF16 ? D + 16 : D + 4;      // V row pitch
+  static constexpr int QSTEPS = kBF16 ? D / 16 : D / 2;  // MFMA k-steps over D
+  static constexpr int TILE_INST = 2 * N * CPR / 64;     // K+V wave loads per tile
+  static constexpr int HALF_INST = TILE_INST / 2;
+  static constexpr int KPI = 64 / CPR;                   // keys per wave load
+  static constexpr int KV_PER = (TILE_INST + kPrefillWaves - 1) / kPrefillWaves;
+  static constexpr int SBC_MAX = (N + VEC) / VEC;        // bias chunks per row
+  static constexpr int BIAS_PER = (32 * SBC_MAX + 63) / 64;
   using QOp = typename std::conditional<kBF16, bf16x8, float>::type;
-  static constexpr size_t tile_bytes() {
-    return (size_t)(N * KP + D * VP) * sizeof(T);
-  }
+  static constexpr size_t stage_bytes() { return (size_t)(N * KP + N * VP) * sizeof(T); }
 };
 
 template <typename T>
-__device__ __forceinline__ void store4(T* dst, float a, float b, float c,
-                                       float d) {
+__device__ __forceinline__ void store4(T* dst, float a, float b, float c, float d) {
   if constexpr (sizeof(T) == 2) {
-    bf16x4 v = {from_f32<bf16>(a), from_f32<bf16>(b), from_f32<bf16>(c),
-                from_f32<bf16>(d)};
+    bf16x4 v = {from_f32<bf16>(a), from_f32<bf16>(b), from_f32<bf16>(c), from_f32<bf16>(d)};
     *reinterpret_cast<bf16x4*>(dst) = v;
   } else {
     *reinterpret_cast<f32x4*>(dst) = f32x4{a, b, c, d};
   }
 }
 
+// Workgroup barrier that orders LDS only: in-flight global loads of the
+// issuing waves are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <typename T, int D>
-__global__ void __launch_bounds__(768)
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_kernel(const PrefillParams P) {
   using C = Prefill<T, D>;
-  constexpr int N = C::N, VEC = C::VEC, KP = C::KP, VP = C::VP;
-  constexpr int CPR = D / VEC;  // 16-byte chunks per K/V row
+  constexpr int N = C::N, VEC = C::VEC, CPR = C::CPR, KP = C::KP, VP = C::VP, KPI = C::KPI;
+  constexpr uint32_t SZ = sizeof(T);
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  T* Ks = reinterpret_cast<T*>(smem);
-  T* Vt = Ks + N * KP;
-  unsigned char* Bs = smem + C::tile_bytes();
 
-  const T* __restrict__ qg = static_cast<const T*>(P.q);
-  const T* __restrict__ kg = static_cast<const T*>(P.k);
-  const T* __restrict__ vg = static_cast<const T*>(P.v);
-  const T* __restrict__ rg = static_cast<const T*>(P.rel);
-  T* __restrict__ og = static_cast<T*>(P.out);
-
-  const int b = blockIdx.y, g = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nthr = blockDim.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  constexpr int nw = kPrefillWaves;
   const int G = P.group, bq = P.bq, R = P.rel_len, SB = P.sb, W = P.window;
   const int64_t hq = P.hq;
+
+  // XCD-aware work index: workgroup id x runs on XCD x % 8; give each XCD
+  // a contiguous range of work (query block fastest, heaviest first).
+  const int total = P.nqb * P.num_seqs * P.hkv;
+  const int per_xcd = (total + 7) >> 3;
+  const int w = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (w >= total) return;
+  const int qb = P.nqb - 1 - w % P.nqb;
+  const int bg = w / P.nqb;
+  const int b = bg % P.num_seqs, g = bg / P.num_seqs;
 
   // Sequence metadata, clamped so that no read leaves the arguments.
   const int q0 = iclamp(P.cu_q_lens[b], 0, P.total_q);
   const int q1 = iclamp(P.cu_q_lens[b + 1], q0, P.total_q);
   const int L = iclamp(P.seq_lens[b], 0, P.max_blocks * 16);
   const int n = imin(q1 - q0, L);
-  // Later token blocks see more keys under full causal attention: start
-  // them first.
-  const int t0 = (gridDim.x - 1 - blockIdx.x) * bq;
+  const int t0 = qb * bq;
   if (t0 >= n) return;
   const int tend = imin(t0 + bq, n);
-  const int pbase = L - n;  // position of token 0 of this sequence
-  const int jb = W > 0 ? imax(0, pbase + t0 - W + 1) : 0;  // block's first key
-  const int je = pbase + tend;                              // one past last
+  const int pbase = L - n;                                  // position of token 0
+  const int jb = W > 0 ? imax(0, pbase + t0 - W + 1) : 0;   // block's first key
+  const int je = pbase + tend;                              // one past last key
 
   // This lane's column (query head, token).
   const int col = lane & 31, u = lane >> 5;
@@ -101,219 +133,353 @@ prefill_kernel(const PrefillParams P) {
   const bool cval = hh < G && tc < tend;
   const int h = g * G + (hh < G ? hh : 0);
   const int pc = pbase + tc;
-  // The wave's token range and visible key range.
-  const int wt_lo = bq >= 32 ? t0 + (wave * 32) % bq : t0;
-  const int wt_hi = imin(wt_lo + (bq >= 32 ? 32 : bq), tend);  // exclusive
-  const bool wact = wt_lo < tend && (wave * 32) / bq < G;
+  // The wave's token range (a wave may straddle two heads, then it covers
+  // every token of the block) and its visible key range.
+  const int c_lo = wave * 32, c_hi = imin(c_lo + 31, G * bq - 1);
+  const bool one_head = c_lo / bq == c_hi / bq;
+  const int wt_lo = one_head ? t0 + c_lo % bq : t0;
+  const int wt_hi = imin(one_head ? t0 + c_hi % bq + 1 : t0 + bq, tend);   // exclusive
+  const bool wact = c_lo < G * bq && wt_lo < tend;
   const int wjb = W > 0 ? imax(0, pbase + wt_lo - W + 1) : 0;
   const int wje = pbase + wt_hi;
 
-  typename C::QOp qop[C::QSTEPS];
-  if constexpr (C::kBF16) {
-    const bf16* src = qg + ((int64_t)(q0 + tc) * hq + h) * D + 8 * u;
-#pragma unroll
-    for (int s = 0; s < C::QSTEPS; ++s)
-      qop[s] = cval ? *reinterpret_cast<const bf16x8*>(src + 16 * s) : bf16x8{};
-  } else {
-    const float* src = qg + ((int64_t)(q0 + tc) * hq + h) * D + u;
-#pragma unroll
-    for (int s = 0; s < C::QSTEPS; ++s) qop[s] = cval ? src[2 * s] : 0.f;
+  // LDS: two stages of (K tile, V tile), per-wave bias runs (two stages),
+  // then the page-id table.
+  auto stage = [&](int st) { return reinterpret_cast<T*>(smem + st * C::stage_bytes()); };
+  unsigned char* bias_lds = smem + 2 * C::stage_bytes();
+  const int sbp = P.sb_pitch;
+  int* pid_lds = reinterpret_cast<int*>(bias_lds + (size_t)nw * 2 * 32 * sbp);
+
+  // Page ids of keys [jb, je).
+  const int pg_lo = jb >> 4;
+  const int npg = imin(((je - 1) >> 4) - pg_lo + 1, P.pid_cap);
+  {
+    const int seq_pages = (L + 15) >> 4;
+    const __amdgpu_buffer_rsrc_t bt_rsrc =
+        make_rsrc(P.block_table + (int64_t)b * P.max_blocks, (uint32_t)seq_pages * 4u);
+    for (int i = tid; i < npg; i += blockDim.x)
+      pid_lds[i] = iclamp((int)bload32(bt_rsrc, (uint32_t)(pg_lo + i) * 4u), 0, P.num_blocks - 1);
   }
+
+  typename C::QOp qop[C::QSTEPS];
+  {
+    const T* qg = static_cast<const T*>(P.q);
+    if constexpr (C::kBF16) {
+      const bf16* src = qg + ((int64_t)(q0 + tc) * hq + h) * D + 8 * u;
+#pragma unroll
+      for (int s = 0; s < C::QSTEPS; ++s)
+        qop[s] = cval ? *reinterpret_cast<const bf16x8*>(src + 16 * s) : bf16x8{};
+    } else {
+      const float* src = qg + ((int64_t)(q0 + tc) * hq + h) * D + u;
+#pragma unroll
+      for (int s = 0; s < C::QSTEPS; ++s) qop[s] = cval ? src[2 * s] : 0.f;
+    }
+  }
+
+  const uint32_t slot_bytes = (uint32_t)P.hkv * D * SZ;
+  const uint32_t page_bytes = 16u * slot_bytes;
+  const uint32_t head_bytes = (uint32_t)g * D * SZ;
+  const char* kg = static_cast<const char*>(P.k);
+  const char* vg = static_cast<const char*>(P.v);
+  // Bias rows of tokens [t0, tend), all heads: row (t, h') at
+  // ((t - t0) * Hq + h') * R.
+  const __amdgpu_buffer_rsrc_t rel_rsrc =
+      make_rsrc(static_cast<const T*>(P.rel) + (int64_t)(q0 + t0) * hq * R,
+                (uint32_t)(tend - t0) * (uint32_t)hq * (uint32_t)R * SZ);
+  const int sbc = SB / VEC;  // bias chunks per row
+
+  // ---- loads of one tile into registers ---------------------------------
+  struct Regs {
+    uint4 kv[C::KV_PER];
+    uint4 b[C::BIAS_PER];
+  };
+  // Lane constants of the loads (independent of the tile).  K/V load i of
+  // this wave: keys kk_i .. kk_i + KPI of the tile, lane -> key kk_i +
+  // lane / CPR, 16-byte chunk lane % CPR; tiles start at multiples of 16,
+  // so the slot of the key inside its page is fixed.
+  uint32_t kv_lane[C::KV_PER];
+#pragma unroll
+  for (int i = 0; i < C::KV_PER; ++i) {
+    const int k = wave + nw * i;
+    const int kk = (k >= C::HALF_INST ? k - C::HALF_INST : k) * KPI;
+    kv_lane[i] = (uint32_t)((kk + lane / CPR) & 15) * slot_bytes + head_bytes +
+                 (uint32_t)(lane % CPR) * 16u;
+  }
+  // Bias load i: row r = c / sbc (token rt, head rh), chunk c % sbc.
+  uint32_t b_row[C::BIAS_PER];   // row offset | 0x80000000 if the row is unused
+  int b_pos[C::BIAS_PER];        // position of the row's token + (part * VEC << 20)
+#pragma unroll
+  for (int i = 0; i < C::BIAS_PER; ++i) {
+    const int c = i * 64 + lane;
+    const int r = c / sbc, part = c - r * sbc;
+    const int rc = wave * 32 + r;
+    const int rh = rc / bq, rt = t0 + rc % bq;
+    const bool ok = r < 32 && rh < G && rt < tend;
+    b_row[i] = ((uint32_t)((rt - t0) * hq + g * G + rh) * (uint32_t)R + (uint32_t)(part * VEC)) * SZ |
+               (ok ? 0u : kOOB);
+    b_pos[i] = pbase + rt;
+  }
+  // Loads of tile kt.  Keys outside [jb, je) and rows the wave does not
+  // stage read as kOOB (zero, no memory traffic); no control flow.
+  auto issue = [&](Regs& rg, int kt) {
+#pragma unroll
+    for (int i = 0; i < C::KV_PER; ++i) {
+      const int k = wave + nw * i;                        // wave-uniform
+      const bool is_v = k >= C::HALF_INST;
+      const int kk = (is_v ? k - C::HALF_INST : k) * KPI;
+      const int blk = iclamp(((kt + kk) >> 4) - pg_lo, 0, P.pid_cap - 1);
+      const int64_t page = __builtin_amdgcn_readfirstlane(pid_lds[blk]);
+      const __amdgpu_buffer_rsrc_t r =
+          make_rsrc((is_v ? vg : kg) + page * page_bytes, page_bytes);
+      const int j = kt + kk + lane / CPR;
+      const bool ok = k < C::TILE_INST && (uint32_t)(j - jb) < (uint32_t)(je - jb);
+      rg.kv[i] = bload128(r, kv_lane[i] | (ok ? 0u : kOOB));
+    }
+    const bool wtile = wact && kt < wje && kt + N > wjb;  // wave-uniform
+#pragma unroll
+    for (int i = 0; i < C::BIAS_PER; ++i) {
+      // Distances [p - kt - N + 1, p - kt] clamped to R - 1 lie in the
+      // aligned window [base, base + SB).
+      const int base = iclamp(floor_to(b_pos[i] - kt - (N - 1), VEC), 0, R - SB);
+      const uint32_t off = b_row[i] + (uint32_t)base * SZ;
+      rg.b[i] = bload128(rel_rsrc, wtile ? off : kOOB);
+    }
+  };
+  auto commit = [&](const Regs& rg, int st) {
+    T* Ks = stage(st);
+    T* Vs = Ks + N * KP;
+#pragma unroll
+    for (int i = 0; i < C::KV_PER; ++i) {
+      const int k = wave + nw * i;
+      if (k < C::TILE_INST) {                             // wave-uniform
+        const bool is_v = k >= C::HALF_INST;
+        const int key = (is_v ? k - C::HALF_INST : k) * KPI + lane / CPR;
+        const int part = lane % CPR;
+        if (is_v) {
+          *reinterpret_cast<uint4*>(Vs + key * VP + part * VEC) = rg.kv[i];
+        } else {
+          *reinterpret_cast<uint4*>(Ks + key * KP + part * VEC) = rg.kv[i];
+        }
+      }
+    }
+    unsigned char* Bw = bias_lds + (size_t)(wave * 2 + st) * 32 * sbp;
+#pragma unroll
+    for (int i = 0; i < C::BIAS_PER; ++i) {
+      const int c = i * 64 + lane;
+      const int r = c / sbc, part = c - r * sbc;
+      if (r < 32) {
+        uint32_t* dst = reinterpret_cast<uint32_t*>(Bw + r * sbp + part * 16);
+        dst[0] = rg.b[i].x;
+        dst[1] = rg.b[i].y;
+        dst[2] = rg.b[i].z;
+        dst[3] = rg.b[i].w;
+      }
+    }
+  };
 
   f32x16 acc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
-  float m_run = kNegInf, l_run = 0.f;
+  float m_ref = kNegInf;   // reference max of the logits
+  float l_run = 0.f;
 
-  const int64_t bt_row = (int64_t)b * P.max_blocks;
-  const int sbp = P.sb_pitch;
-  const int bias_cpr = SB / VEC;
-
-  for (int kt = jb & ~15; kt < je; kt += N) {
-    __syncthreads();  // previous tile fully consumed
-    // K tile, row-major: consecutive lanes read consecutive 16-byte chunks.
-    for (int c = tid; c < N * CPR; c += nthr) {
-      const int kk = c / CPR, part = c - kk * CPR;
-      const int j = kt + kk;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (j >= jb && j < je) {
-        const int page = iclamp(P.block_table[bt_row + (j >> 4)], 0, P.num_blocks - 1);
-        val = *reinterpret_cast<const uint4*>(
-            kg + (((int64_t)page * 16 + (j & 15)) * P.hkv + g) * D + part * VEC);
-      }
-      *reinterpret_cast<uint4*>(Ks + kk * KP + part * VEC) = val;
-    }
-    // V tile, transposed to V^T[d][key]: lanes take consecutive keys so each
-    // LDS store writes one contiguous run of a V^T row.
-    for (int c = tid; c < N * CPR; c += nthr) {
-      const int kk = c % N, part = c / N;
-      const int j = kt + kk;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (j >= jb && j < je) {
-        const int page = iclamp(P.block_table[bt_row + (j >> 4)], 0, P.num_blocks - 1);
-        val = *reinterpret_cast<const uint4*>(
-            vg + (((int64_t)page * 16 + (j & 15)) * P.hkv + g) * D + part * VEC);
-      }
-      const T* e = reinterpret_cast<const T*>(&val);
-#pragma unroll
-      for (int x = 0; x < VEC; ++x) Vt[(part * VEC + x) * VP + kk] = e[x];
-    }
-    // Bias runs of this wave's rows: distances [p - kt - N + 1, p - kt],
-    // clamped to R - 1, taken from an aligned window of SB entries.
-    const bool wtile = wact && kt < wje && kt + N > wjb;
-    if (wtile) {
-      unsigned char* Bw = Bs + wave * 32 * sbp;
-      for (int c = lane; c < 32 * bias_cpr; c += 64) {
-        const int r = c / bias_cpr, part = c - r * bias_cpr;
-        const int rc = wave * 32 + r;
-        const int rh = rc / bq, rt = t0 + rc % bq;
-        uint4 val = make_uint4(0, 0, 0, 0);
-        if (rh < G && rt < tend) {
-          const int base = iclamp(floor_to(pbase + rt - kt - (N - 1), VEC), 0, R - SB);
-          val = *reinterpret_cast<const uint4*>(
-              rg + ((int64_t)(q0 + rt) * hq + g * G + rh) * R + base + part * VEC);
-        }
-        uint32_t* dst = reinterpret_cast<uint32_t*>(Bw + r * sbp + part * 16);
-        dst[0] = val.x;
-        dst[1] = val.y;
-        dst[2] = val.z;
-        dst[3] = val.w;
-      }
-    }
-    __syncthreads();
-    if (!wtile) continue;
-
-    const T* brow = reinterpret_cast<const T*>(Bs + (wave * 32 + col) * sbp);
+  // ---- compute one tile from LDS stage st --------------------------------
+  auto compute = [&](int kt, int st) {
+    if (!(wact && kt < wje && kt + N > wjb)) return;      // wave-uniform
+    const T* Ks = stage(st);
+    const T* Vs = Ks + N * KP;
+    const T* brow = reinterpret_cast<const T*>(bias_lds + (size_t)(wave * 2 + st) * 32 * sbp +
+                                               col * sbp);
     const int base_c = iclamp(floor_to(pc - kt - (N - 1), VEC), 0, R - SB);
+    f32x16 s = f32x16{};
+    if constexpr (C::kBF16) {
+      const bf16* krow = Ks + col * KP + 8 * u;
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      const int kb = kt + 32 * kh;
-      if (kb >= wje || kb + 32 <= wjb) continue;  // wave-uniform
-      // S^T for 32 keys x 32 columns.
-      f32x16 s = f32x16{};
-      if constexpr (C::kBF16) {
-        const bf16* krow = Ks + (32 * kh + col) * KP + 8 * u;
+      for (int st2 = 0; st2 < C::QSTEPS; ++st2)
+        s = mfma32(*reinterpret_cast<const bf16x8*>(krow + 16 * st2), qop[st2], s);
+    } else {
+      const float* krow = Ks + col * KP + u;
 #pragma unroll
-        for (int st = 0; st < C::QSTEPS; ++st)
-          s = mfma32(*reinterpret_cast<const bf16x8*>(krow + 16 * st), qop[st], s);
-      } else {
-        const float* krow = Ks + (32 * kh + col) * KP + u;
+      for (int st2 = 0; st2 < C::QSTEPS; ++st2) s = mfma32(krow[2 * st2], qop[st2], s);
+    }
+    // x = scale * S + bias (natural-log units); lane holds keys
+    // kt + 8*(i/4) + 4*u + i%4, i.e. distances d_i = pc - kt - 4u - c_i with
+    // c_i = 8*(i/4) + i%4.
+    float x[16];
+    float mx = kNegInf;
+    // Element i sits at distance d_i = D0 - c_i, D0 = pc - kt - 4u,
+    // c_i = 8*(i/4) + i%4 (compile-time), and its bias at offset d_i -
+    // base_c of the staged run: one base per lane plus immediate offsets.
+    // Tiles with no distance at the clamp read the run directly and mask by
+    // select (only on tiles that cross the window or causal boundary);
+    // tiles that reach the clamp take the general path.
+    const int D0 = pc - kt - 4 * u;
+    const bool unclamped = (wje - 1) - kt <= R - 1;       // wave-uniform
+    const bool full = (W <= 0 || (wje - 1) - kt < W) && (pbase + wt_lo) - (kt + N - 1) >= 0;
+    if (unclamped) {
+      const T* bb = brow + (D0 - base_c - 27);
 #pragma unroll
-        for (int st = 0; st < C::QSTEPS; ++st) s = mfma32(krow[2 * st], qop[st], s);
+      for (int i = 0; i < 16; ++i)
+        x[i] = fmaf(s[i], P.scale, to_f32(bb[27 - (8 * (i >> 2) + (i & 3))]));
+      if (!full) {                                        // wave-uniform
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int d = D0 - (8 * (i >> 2) + (i & 3));
+          const bool vis = d >= 0 && (W <= 0 || d < W);
+          x[i] = vis ? x[i] : kNegInf;
+        }
       }
-      // Scale, bias, mask; lane holds keys kb + 8*(i/4) + 4*u + i%4.
-      float x[16];
-      float mx = kNegInf;
+    } else {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int j = kb + 8 * (i >> 2) + 4 * u + (i & 3);
-        const int d = pc - j;
-        const bool vis = cval && d >= 0 && (W <= 0 || d < W);
+        const int d = D0 - (8 * (i >> 2) + (i & 3));
+        // di is always inside the staged run, so the read is unconditional.
         const int di = iclamp(imin(d, R - 1) - base_c, 0, SB - 1);
-        const float bias = to_f32(brow[di]);
-        x[i] = vis ? fmaf(s[i], P.scale, bias) : kNegInf;
-        mx = fmaxf(mx, x[i]);
+        const float bv = to_f32(brow[di]);
+        const bool vis = d >= 0 && (W <= 0 || d < W);
+        x[i] = vis ? fmaf(s[i], P.scale, bv) : kNegInf;
       }
-      mx = fmaxf(mx, xor_lane(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = fast_exp2((m_run - m_use) * kLog2e);
-      m_run = m_new;
-      const float mb = m_use * kLog2e;
-      float lsum = 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, x[i]);
+    mx = fmaxf(mx, xor_lane(mx, 32));
+    // Move the reference max only when this tile exceeds it by > kLazy
+    // (in log2 units), so that P <= 2^kLazy.
+    const bool move = mx > m_ref + kLazy * kLn2;
+    if (__builtin_amdgcn_ballot_w64(move)) {              // wave-uniform
+      const float m_new = move ? mx : m_ref;
+      const float alpha = move ? fast_exp2((m_ref - m_new) * kLog2e) : 1.f;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= alpha;
-      if constexpr (C::kBF16) {
-        // P rounded to bf16; the row sum uses the rounded values so the
-        // weights applied to V are exactly normalised.
-        bf16x8 pb[2];
+      l_run *= alpha;
+      m_ref = m_new;
+    }
+    const float mb = m_ref == kNegInf ? 0.f : m_ref * kLog2e;
+    if constexpr (C::kBF16) {
+      bf16x8 pb[2];
+      const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const bf16 r = from_f32<bf16>(fast_exp2(fmaf(x[i], kLog2e, -mb)));
-          pb[i >> 3][i & 7] = r;
-          lsum += to_f32(r);
-        }
+      for (int i = 0; i < 16; i += 2) {
+        const bf16x2 pr = {from_f32<bf16>(fast_exp2(fmaf(x[i], kLog2e, -mb))),
+                           from_f32<bf16>(fast_exp2(fmaf(x[i + 1], kLog2e, -mb)))};
+        pb[i >> 3][i & 7] = pr[0];
+        pb[i >> 3][(i & 7) + 1] = pr[1];
+        // The row sum uses the rounded values, so the weights applied to V
+        // are exactly normalised.
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
+      }
+      // V^T operand for 16 keys ks*16 + slots (u, e): keys 16ks + 4u + e
+      // (e < 4) and 16ks + 8 + 4u + e - 4 (e >= 4), matching pb[ks].  The
+      // 16-lane groups of a transposed read cover d0..d0+15: lane j points
+      // at key (4u + j/4), columns d0 + 4*(j%4) .. +3.
+      const int jj = lane & 15;
+      const int dgrp = (lane >> 4) & 1;
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          const bf16* vrow = Vt + (32 * dt + col) * VP + 32 * kh + 4 * u;
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const T* vb = Vs + (4 * u + (jj >> 2)) * VP + 32 * dt + 16 * dgrp + 4 * (jj & 3);
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vrow + 16 * ks);
-            const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vrow + 16 * ks + 8);
-            const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            acc[dt] = mfma32(a, pb[ks], acc[dt]);
-          }
-        }
-      } else {
-        float pf[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          pf[i] = fast_exp2(fmaf(x[i], kLog2e, -mb));
-          lsum += pf[i];
-        }
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          const float* vrow = Vt + (32 * dt + col) * VP + 32 * kh + 4 * u;
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            acc[dt] = mfma32(vrow[8 * (i >> 2) + (i & 3)], pf[i], acc[dt]);
+        for (int ks = 0; ks < 2; ++ks) {
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(vb + (16 * ks) * VP));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(vb + (16 * ks + 8) * VP));
+          const i16x8 a16 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          acc[dt] = mfma32(__builtin_bit_cast(bf16x8, a16), pb[ks], acc[dt]);
         }
       }
-      l_run = l_run * alpha + lsum;
+    } else {
+      float pf[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        pf[i] = fast_exp2(fmaf(x[i], kLog2e, -mb));
+        l_run += pf[i];
+      }
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const float* vrow = Vs + 4 * u * VP + 32 * dt + col;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          acc[dt] = mfma32(vrow[(8 * (i >> 2) + (i & 3)) * VP], pf[i], acc[dt]);
+      }
     }
+  };
+
+  // ---- software pipeline over key tiles ----------------------------------
+  // Two register buffers keep two tiles in flight: at the top of each step
+  // tile kt sits in an LDS stage, tile kt+N in one buffer (issued a step
+  // earlier) and tile kt+2N is issued into the other.  Loads past the last
+  // tile are kOOB no-ops, so no load sits under control flow.
+  lds_barrier();                                         // page ids ready
+  int kt = jb & ~15;
+  Regs ra, rb;
+  issue(ra, kt);
+  issue(rb, kt + N);
+  commit(ra, 0);
+  lds_barrier();
+  while (true) {
+    issue(ra, kt + 2 * N);
+    compute(kt, 0);
+    if (kt + N >= je) break;                             // workgroup-uniform
+    commit(rb, 1);
+    lds_barrier();
+    kt += N;
+    issue(rb, kt + 2 * N);
+    compute(kt, 1);
+    if (kt + N >= je) break;
+    commit(ra, 0);
+    lds_barrier();
+    kt += N;
   }
 
   if (!wact) return;
   const float lt = l_run + xor_lane(l_run, 32);
   if (!cval) return;
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  T* dst = og + ((int64_t)(q0 + tc) * hq + h) * D;
+  T* dst = static_cast<T*>(P.out) + ((int64_t)(q0 + tc) * hq + h) * D;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4)
-      store4(dst + 32 * dt + 8 * q4 + 4 * u, acc[dt][4 * q4] * inv,
-             acc[dt][4 * q4 + 1] * inv, acc[dt][4 * q4 + 2] * inv,
-             acc[dt][4 * q4 + 3] * inv);
+      store4(dst + 32 * dt + 8 * q4 + 4 * u, acc[dt][4 * q4] * inv, acc[dt][4 * q4 + 1] * inv,
+             acc[dt][4 * q4 + 2] * inv, acc[dt][4 * q4 + 3] * inv);
 }
 
 template <typename T, int D>
-hipError_t launch_t(const PrefillParams& p, int num_seqs, int max_q_len,
-                    hipStream_t stream) {
-  const int waves = (p.group * p.bq + 31) / 32;
-  const size_t lds = Prefill<T, D>::tile_bytes() + (size_t)waves * 32 * p.sb_pitch;
+size_t lds_bytes_t(int waves, int sb_pitch, int pid_cap) {
+  return 2 * Prefill<T, D>::stage_bytes() + (size_t)waves * 2 * 32 * sb_pitch +
+         (size_t)pid_cap * 4;
+}
+
+template <typename T, int D>
+hipError_t launch_t(const PrefillParams& p, hipStream_t stream) {
+  const size_t lds = lds_bytes_t<T, D>(kPrefillWaves, p.sb_pitch, p.pid_cap);
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&prefill_kernel<T, D>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<T, D>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const dim3 grid((max_q_len + p.bq - 1) / p.bq, num_seqs, p.hkv);
-  prefill_kernel<T, D><<<grid, dim3(waves * 64), lds, stream>>>(p);
+  const int64_t total = (int64_t)p.nqb * p.num_seqs * p.hkv;
+  const int64_t grid = ((total + 7) / 8) * 8;
+  prefill_kernel<T, D><<<dim3((unsigned)grid), dim3(kPrefillWaves * 64), lds, stream>>>(p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t prefill_lds_bytes(int dtype, int head_dim, int waves, int sb_pitch) {
-  size_t tile = 0;
+size_t prefill_lds_bytes(int dtype, int head_dim, int waves, int sb_pitch, int pid_cap) {
   if (dtype == 0)
-    tile = head_dim == 64 ? Prefill<bf16, 64>::tile_bytes() : Prefill<bf16, 128>::tile_bytes();
-  else
-    tile = head_dim == 64 ? Prefill<float, 64>::tile_bytes() : Prefill<float, 128>::tile_bytes();
-  return tile + (size_t)waves * 32 * sb_pitch;
+    return head_dim == 64 ? lds_bytes_t<bf16, 64>(waves, sb_pitch, pid_cap)
+                          : lds_bytes_t<bf16, 128>(waves, sb_pitch, pid_cap);
+  return head_dim == 64 ? lds_bytes_t<float, 64>(waves, sb_pitch, pid_cap)
+                        : lds_bytes_t<float, 128>(waves, sb_pitch, pid_cap);
 }
 
-hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim,
-                          int num_seqs, int max_q_len, hipStream_t stream) {
-  if (dtype == 0) {
-    return head_dim == 64 ? launch_t<bf16, 64>(p, num_seqs, max_q_len, stream)
-                          : launch_t<bf16, 128>(p, num_seqs, max_q_len, stream);
-  }
-  return head_dim == 64 ? launch_t<float, 64>(p, num_seqs, max_q_len, stream)
-                        : launch_t<float, 128>(p, num_seqs, max_q_len, stream);
+hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim, hipStream_t stream) {
+  if (dtype == 0)
+    return head_dim == 64 ? launch_t<bf16, 64>(p, stream) : launch_t<bf16, 128>(p, stream);
+  return head_dim == 64 ? launch_t<float, 64>(p, stream) : launch_t<float, 128>(p, stream);
 }
 
 }  // namespace ira
