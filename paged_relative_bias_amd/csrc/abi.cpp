@@ -54,15 +54,30 @@ int device_cus(int32_t device) {
   return 256;
 }
 
+// 32-key tiles a decode wave may have to cover for one sequence: the visible
+// keys (the window on local layers, the whole context on global ones) plus
+// up to 15 keys of alignment to the first page.
+int64_t decode_max_tiles(const inkling_rel_attn_dims_t* d, int32_t window) {
+  const int64_t keys = window > 0 ? std::min<int64_t>(window, d->max_seq_len)
+                                  : (int64_t)d->max_seq_len;
+  return std::max<int64_t>(1, (keys + 15 + kDecodeKeys - 1) / kDecodeKeys);
+}
+
+// Tiles per split for a given split count: sequence b then uses
+// ceil(tiles_b / chunk) <= num_splits splits.
+int32_t decode_chunk_tiles(const inkling_rel_attn_dims_t* d, int32_t window, int32_t splits) {
+  const int64_t t = decode_max_tiles(d, window);
+  return (int32_t)((t + splits - 1) / splits);
+}
+
 int32_t splits_for(const inkling_rel_attn_dims_t* d, int32_t window, int cus) {
   const int64_t units = (int64_t)d->num_seqs * d->num_kv_heads;
   if (units <= 0) return 1;
-  const int64_t keys = window > 0 ? std::min<int64_t>(window, d->max_seq_len)
-                                  : (int64_t)d->max_seq_len;
-  // Aim for about two workgroups per compute unit, but keep at least 256
-  // keys (eight wave tiles, two per wave) in every split.
-  const int64_t want = (2LL * cus + units - 1) / units;
-  const int64_t cap = std::max<int64_t>(1, keys / 256);
+  // One wave per (sequence, KV head, split); aim for one wave per SIMD of
+  // the device, keeping at least 8 tiles (256 keys) in every split.
+  const int64_t tiles = decode_max_tiles(d, window);
+  const int64_t want = ((int64_t)kDecodeWavesPerCU * cus + units - 1) / units;
+  const int64_t cap = std::max<int64_t>(1, tiles / 8);
   int64_t s = std::min<int64_t>(want, cap);
   s = std::max<int64_t>(1, std::min<int64_t>(s, kMaxSplits));
   return (int32_t)s;
@@ -251,7 +266,21 @@ inkling_status_t inkling_rel_attn_decode(const void* q, const void* k_cache, con
   p.rel_len = dims->rel_len;
   p.window = window;
   p.num_splits = num_splits;
+  p.chunk_tiles = decode_chunk_tiles(dims, window, num_splits);
+  p.pid_cap = 2 * p.chunk_tiles + 16;
+  p.max_seq_len = dims->max_seq_len;
   p.scale = scale;
+  // A visible distance exceeds R - 1 only when the window (or, on global
+  // layers, the longest context) is longer than the bias.
+  const int64_t max_vis_d = window > 0 ? (int64_t)window - 1 : (int64_t)dims->max_seq_len - 1;
+  p.clamp = max_vis_d > dims->rel_len - 1 ? 1 : 0;
+  const size_t esz = dtype_size(dims->dtype);
+  if (decode_lds_bytes(p, dims->dtype, dims->head_dim) > 160 * 1024)
+    return INKLING_ERR_UNSUPPORTED;
+  // 32-bit buffer offsets: one page, and the bias rows of one KV head.
+  if ((int64_t)16 * dims->num_kv_heads * dims->head_dim * (int64_t)esz >= (1LL << 31) ||
+      (int64_t)p.group * dims->rel_len * (int64_t)esz >= (1LL << 30))
+    return INKLING_ERR_UNSUPPORTED;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = launch_decode(p, dims->dtype, dims->head_dim, s);
   if (e != hipSuccess) return INKLING_ERR_LAUNCH;

@@ -7,29 +7,34 @@
 // the split-KV decode the vLLM page describes (section "Changes": up to 128
 // splits, with a helper that picks the count).
 //
-// Work decomposition.  Grid (split, sequence, KV head); 4 waves per
-// workgroup, each owning a contiguous run of 32-key tiles of the split.
-// The G query heads of the KV head are the MFMA columns (G <= 16).
+// Work decomposition.  One wave per (KV head g, split, sequence b); the G
+// query heads of the KV head are the MFMA columns (G <= 16).  A split is a
+// run of at most `chunk_tiles` 32-key tiles of the sequence's visible keys,
+// so every wave of a launch streams about the same number of bytes whatever
+// the sequence lengths; sequence b uses ceil(tiles_b / chunk_tiles) splits
+// and the waves beyond that only mark their partial empty.
 //
-// The kernel is bound by HBM bandwidth, so the loop is built to keep loads
-// in flight:
-//   * each wave reads the page ids of its range once (one page per lane)
-//     and takes them with readlane, so no tile waits on the block table;
-//   * K, V and bias loads for tile t+1 are issued before tile t is
-//     computed (two register buffers, loop unrolled by two);
-//   * K is read straight into MFMA A-operand registers (16 keys x 64 bytes
-//     per instruction); V is read as whole 256-byte rows and written to a
-//     wave-private LDS tile whose 288-byte pitch keeps the transposed reads
-//     free of bank conflicts.
-// Per tile: S^T[key][head] = K . Q^T (16x16x32 bf16 MFMA); scale, bias,
-// mask by select; online softmax with the column max shared across the
-// four lanes of a column; O^T[d][head] += V^T . P^T where the V^T operand
-// comes from ds_read_tr16_b64 (16 lanes each point at 4 consecutive d of
-// one key; lane i receives that d-column for 4 keys) and P^T stays in
-// registers.  The four waves' states are merged through LDS.  With one
-// split the workgroup writes the output; otherwise it writes its
-// normalised partial and log-sum-exp for combine_kernel, which merges the
-// splits in a fixed order (no atomics, bit-reproducible).
+// The kernel is bound by HBM bandwidth; the loop keeps DEPTH tiles of K, V
+// and bias loads in flight in a ring of register buffers:
+//   * the page ids of the split are copied once into LDS; a tile's two page
+//     ids are one broadcast LDS read, taken to SGPRs;
+//   * every K/V load goes through a per-page buffer descriptor whose size
+//     stops at the split's last key, so keys past the end (and whole tiles
+//     past the last one) read zero without any per-lane test or traffic,
+//     and each lane's offset inside a page is a loop constant;
+//   * the bias of the tile is eight 2-byte loads, one per key of the lane
+//     (distances p - j), with out-of-range offsets for keys past the query;
+//   * K is loaded straight into MFMA A-operand registers; V rows are
+//     written to a wave-private LDS tile and read back transposed with
+//     ds_read_tr16_b64.
+// Per tile: S^T[key][head] = K . Q^T (16x16x32 bf16 MFMA); x = scale * S +
+// bias; masking by select only on the first and last tile of the split;
+// online softmax whose reference max moves only when a column's logits
+// exceed it by more than 2^8 (in exp2 units), so the common tile needs no
+// cross-lane exchange; P rounded to bf16 with its row sum taken from the
+// rounded values; O^T[d][head] += V^T . P^T.  One split writes the output;
+// otherwise each wave writes its normalised partial and log-sum-exp, and
+// combine_kernel merges them in split order (no atomics).
 #include <type_traits>
 
 #include "device.hpp"
@@ -39,80 +44,130 @@ namespace ira {
 namespace {
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Largest logit excess over the reference (natural units) for which P =
+// exp(x - m_ref) and the running sums stay far from fp32 / bf16 overflow.
+constexpr float kOver = 40.f;
 
 template <typename T, int D>
 struct Decode {
   static constexpr bool kBF16 = sizeof(T) == 2;
-  static constexpr int NK = kDecodeKeys;              // keys per wave tile
-  static constexpr int CPR = D * (int)sizeof(T) / 16;  // 16-byte chunks per row
-  static constexpr int VLOADS = NK * CPR / 64;        // V chunk loads per lane
-  static constexpr int VSP = D + 16 / (int)sizeof(T) * 2;  // V row pitch (elements)
-  static constexpr int KSTEPS = kBF16 ? D / 32 : D / 4;    // MFMA k-steps over D
+  static constexpr int NK = kDecodeKeys;                 // keys per tile
+  static constexpr int SZ = (int)sizeof(T);
+  static constexpr int VEC = 16 / SZ;                    // elements per 16 B
+  static constexpr int CPR = D / VEC;                    // 16-byte chunks per row
+  static constexpr int KPL = 64 / CPR;                   // keys per wave load
+  static constexpr int VLD = NK / KPL;                   // K (and V) loads per tile
+  static constexpr int NVOFF = 16 / KPL;                 // distinct offsets per page
+  static constexpr int KP = D + VEC;                     // K row pitch (elements)
+  static constexpr int VSP = kBF16 ? D + 16 : D + 4;     // V row pitch (elements)
+  static constexpr int KSTEPS = kBF16 ? D / 32 : D / 4;  // MFMA k-steps per 16 keys
+  static constexpr int BW = 40;                          // bias entries staged per head
+  static constexpr int BCH = BW / VEC;                   // their 16-byte chunks
+  static constexpr int BLD = (kMaxGroup * BCH + 63) / 64;  // bias loads per tile
+  static constexpr int DEPTH = kBF16 ? 2 : 1;            // tiles in flight
+  static constexpr int NBUF = DEPTH + 1;
   using KOp = typename std::conditional<kBF16, bf16x8, float>::type;
-  static constexpr size_t lds_bytes() {
-    const size_t vbuf = (size_t)kDecodeWaves * NK * VSP * sizeof(T);
-    const size_t merge = (size_t)kDecodeWaves * 16 * (D + 2) * sizeof(float);
-    return vbuf > merge ? vbuf : merge;
-  }
+  static constexpr size_t k_bytes() { return (size_t)NK * KP * SZ; }
+  static constexpr size_t v_bytes() { return (size_t)NK * VSP * SZ; }
+  // Rows for every chunk a bias load writes (lanes past the G heads write
+  // their zeros to rows nobody reads, so the store needs no condition).
+  static constexpr int BROWS = (BLD * 64 + BCH - 1) / BCH;
+  static constexpr size_t b_bytes() { return (size_t)BROWS * BW * SZ; }
+  static constexpr size_t fixed_lds() { return k_bytes() + v_bytes() + b_bytes(); }
 };
 
-// Registers holding one tile's K operands and raw bias values.
+// One tile's loads: K rows, V rows and the heads' bias runs, all as
+// 16-byte chunks.
 template <typename T, int D>
-struct KBuf {
+struct Tile {
   using C = Decode<T, D>;
-  typename C::KOp k[2][C::KSTEPS];
-  uint32_t bias[8];
+  uint4 k[C::VLD];
+  uint4 v[C::VLD];
+  uint4 b[C::BLD];
 };
 
-template <typename T>
-__device__ __forceinline__ float raw_to_f32(uint32_t r) {
-  if constexpr (sizeof(T) == 2) return __builtin_bit_cast(float, r << 16);
-  else return __builtin_bit_cast(float, r);
+// Orders this wave's LDS accesses for the compiler (the hardware keeps one
+// wave's LDS operations in order).
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <typename T, int D>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// CLAMP: some visible distance may exceed R - 1 (window or context longer
+// than the bias), so bias offsets are clamped per element.
+template <typename T, int D, bool CLAMP>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 decode_kernel(const DecodeParams P) {
   using C = Decode<T, D>;
-  constexpr int NK = C::NK, VSP = C::VSP, CPR = C::CPR, VEC = 16 / (int)sizeof(T);
+  constexpr int NK = C::NK, VSP = C::VSP, CPR = C::CPR, VEC = C::VEC, KPL = C::KPL;
+  constexpr int DEPTH = C::DEPTH, NBUF = C::NBUF;
   constexpr uint32_t SZ = sizeof(T);
-  constexpr int kSegTiles = 128;                      // 256 pages per segment
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  // LDS: K tile [NK][KP], V tile [NK][VSP], bias runs [BROWS][BW],
+  // then the split's page-id table.
+  T* Ks = reinterpret_cast<T*>(smem);
+  T* Vs = reinterpret_cast<T*>(smem + C::k_bytes());
+  T* Bs = reinterpret_cast<T*>(smem + C::k_bytes() + C::v_bytes());
+  int* pid_lds = reinterpret_cast<int*>(smem + C::fixed_lds());
 
-  const T* __restrict__ qg = static_cast<const T*>(P.q);
-  const char* kg = static_cast<const char*>(P.k);
-  const char* vg = static_cast<const char*>(P.v);
-  const T* __restrict__ rg = static_cast<const T*>(P.rel);
-
-  // KV head fastest: the workgroups reading the Hkv interleaved rows of
-  // the same pages run side by side.
   const int g = blockIdx.x, split = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = threadIdx.x;
   const int col = lane & 15, u4 = lane >> 4;
   const int G = P.group, R = P.rel_len, W = P.window;
-  const int64_t hq = P.hq;
-  const int hkv = P.hkv;
   const bool cval = col < G;
   const int h = g * G + (cval ? col : 0);
+  const int64_t row = (int64_t)b * P.hq + h;
+  const bool multi = P.num_splits > 1;
 
+  // Keys of this split: tiles [split * CT, split * CT + ntiles) of the
+  // sequence's tiles, which start at the first visible key rounded down to
+  // a page boundary.
   const int L = iclamp(P.seq_lens[b], 0, P.max_blocks * 16);
-  const int pq = L - 1;                               // query position
-  const int k_lo = W > 0 ? imax(0, L - W) : 0;        // first visible key
+  const int pq = L - 1;                                  // query position
+  const int k_lo = W > 0 ? imax(0, L - W) : 0;           // first visible key
   const int kb0 = k_lo & ~15;
-  int chunk = (L - kb0 + P.num_splits - 1) / P.num_splits;
-  chunk = (chunk + NK - 1) & ~(NK - 1);
-  const int s_lo = kb0 + split * chunk;
-  const int s_hi = imin(L, s_lo + chunk);
-  const int v_lo = imax(s_lo, k_lo);                  // keys [v_lo, s_hi)
-  const int ntiles = s_hi > s_lo ? (s_hi - s_lo + NK - 1) / NK : 0;
-  const int tpw = (ntiles + kDecodeWaves - 1) / kDecodeWaves;
-  const int t_begin = imin(ntiles, wave * tpw);
-  const int t_end = imin(ntiles, t_begin + tpw);
+  const int seq_tiles = L > kb0 ? (L - kb0 + NK - 1) / NK : 0;
+  const int CT = P.chunk_tiles;
+  const int ntiles = imin(seq_tiles - split * CT, CT);
+  if (ntiles <= 0) {
+    // Empty split: an empty partial (lse = -inf), or a zero output row when
+    // the sequence has no key at all and there is no merge.
+    if (cval) {
+      if (multi) {
+        if (u4 == 0) P.part_lse[(int64_t)split * P.num_seqs * P.hq + row] = kNegInf;
+      } else {
+        T* dst = static_cast<T*>(P.out) + row * D;
+        for (int d = u4; d < D; d += 4) dst[d] = from_f32<T>(0.f);
+      }
+    }
+    return;
+  }
+  const int s_lo = kb0 + split * CT * NK;
+  const int s_hi = imin(L, s_lo + CT * NK);
+  const int v_lo = imax(s_lo, k_lo);                     // visible keys [v_lo, s_hi)
 
+  // Page ids of the split (and zeros past its end, read by the prefetches
+  // beyond the last tile) into LDS.
+  const int pg_base = s_lo >> 4;
+  const int npg = ((s_hi - 1) >> 4) - pg_base + 1;
+  {
+    const int seq_pages = (L + 15) >> 4;
+    const __amdgpu_buffer_rsrc_t bt_rsrc =
+        make_rsrc(P.block_table + (int64_t)b * P.max_blocks, (uint32_t)seq_pages * 4u);
+    for (int i = lane; i < P.pid_cap; i += 64) {
+      const uint32_t off = i < npg ? (uint32_t)(pg_base + i) * 4u : kOOB;
+      pid_lds[i] = iclamp((int)bload32(bt_rsrc, off), 0, P.num_blocks - 1);
+    }
+  }
+
+  // Q^T operand (B of the QK MFMA): lane holds head col, d = 32 st + 8 u4 ..
   typename C::KOp qop[C::KSTEPS];
   {
-    const T* src = qg + ((int64_t)b * hq + h) * D;
+    const T* src = static_cast<const T*>(P.q) + row * D;
     if constexpr (C::kBF16) {
 #pragma unroll
       for (int s = 0; s < C::KSTEPS; ++s)
@@ -122,145 +177,180 @@ decode_kernel(const DecodeParams P) {
       for (int s = 0; s < C::KSTEPS; ++s) qop[s] = cval ? src[4 * s + u4] : 0.f;
     }
   }
-  // Bias rows of the G heads of this KV head, R entries each.
-  const __amdgpu_buffer_rsrc_t rel_rsrc =
-      make_rsrc(rg + ((int64_t)b * hq + (int64_t)g * G) * R, (uint32_t)(G * R) * SZ);
-  // Block-table row: entries of the sequence's pages only.
-  const int seq_pages = (L + 15) >> 4;
-  const __amdgpu_buffer_rsrc_t bt_rsrc =
-      make_rsrc(P.block_table + (int64_t)b * P.max_blocks, (uint32_t)seq_pages * 4u);
-  // One page holds 16 slots x Hkv heads x D; this head's row of slot s
-  // starts at s * slot_bytes + head_bytes inside it.
-  const uint32_t slot_bytes = (uint32_t)hkv * D * SZ;
+
+  // Loop-constant lane offsets.  A page holds 16 slots x Hkv heads x D.
+  const uint32_t slot_bytes = (uint32_t)P.hkv * D * SZ;
   const uint32_t page_bytes = 16u * slot_bytes;
   const uint32_t head_bytes = (uint32_t)g * D * SZ;
+  const char* kg = static_cast<const char*>(P.k);
+  const char* vg = static_cast<const char*>(P.v);
+  // K and V load i: keys KPL * i + lane / CPR of the tile (slot of the
+  // key's page), 16-byte chunk lane % CPR of the row.
+  uint32_t kv_off[C::NVOFF];
+#pragma unroll
+  for (int j = 0; j < C::NVOFF; ++j)
+    kv_off[j] = (uint32_t)((KPL * j + lane / CPR) & 15) * slot_bytes + head_bytes +
+                (uint32_t)(lane % CPR) * 16u;
+  // Bias: for a tile at kt the keys' distances pq - kt - 31 .. pq - kt lie
+  // in an aligned window [w0, w0 + BW) of each head's row; bias load m
+  // brings chunk (m * 64 + lane) % BCH of head (m * 64 + lane) / BCH.
+  const T* rel_g = static_cast<const T*>(P.rel) + ((int64_t)b * P.hq + (int64_t)g * G) * R;
+  const uint32_t rel_bytes = (uint32_t)(G * R) * SZ;
+  uint32_t b_off[C::BLD];
+#pragma unroll
+  for (int m = 0; m < C::BLD; ++m) {
+    const int idx = m * 64 + lane, hc = idx / C::BCH, ch = idx % C::BCH;
+    b_off[m] = hc < G ? (uint32_t)(hc * R + ch * VEC) * SZ : kOOB;
+  }
+
+  // First entry of the bias window of the tile at kt: the smallest
+  // distance rounded down to a chunk, or (CLAMP) low enough to reach R - 1.
+  auto bias_w0 = [&](int kt) {
+    const int w = floor_to(pq - kt - (NK - 1), VEC);
+    return CLAMP ? imin(w, floor_to(R - NK, VEC)) : w;
+  };
+
+  auto issue = [&](Tile<T, D>& tb, int t) {
+    const int kt = s_lo + t * NK;
+    const int2 pp = *reinterpret_cast<const int2*>(pid_lds + 2 * t);
+    // Descriptor fields must be scalar: readfirstlane keeps every value
+    // below in SGPRs (a VGPR descriptor would need a waterfall loop).
+    const uint64_t p0 = (uint32_t)__builtin_amdgcn_readfirstlane(pp.x);
+    const uint64_t p1 = (uint32_t)__builtin_amdgcn_readfirstlane(pp.y);
+    const uint32_t n0 = sgpr_u32((uint32_t)iclamp(s_hi - kt, 0, 16) * slot_bytes);
+    const uint32_t n1 = sgpr_u32((uint32_t)iclamp(s_hi - kt - 16, 0, 16) * slot_bytes);
+    const __amdgpu_buffer_rsrc_t k0 = make_rsrc(kg + p0 * page_bytes, n0);
+    const __amdgpu_buffer_rsrc_t k1 = make_rsrc(kg + p1 * page_bytes, n1);
+    const __amdgpu_buffer_rsrc_t v0 = make_rsrc(vg + p0 * page_bytes, n0);
+    const __amdgpu_buffer_rsrc_t v1 = make_rsrc(vg + p1 * page_bytes, n1);
+#pragma unroll
+    for (int i = 0; i < C::VLD; ++i)
+      tb.k[i] = bload128((KPL * i) >= 16 ? k1 : k0, kv_off[i % C::NVOFF]);
+#pragma unroll
+    for (int i = 0; i < C::VLD; ++i)
+      tb.v[i] = bload128((KPL * i) >= 16 ? v1 : v0, kv_off[i % C::NVOFF]);
+    // Chunks left of a row start (window of the last tile) get a negative
+    // offset, out of range as an unsigned value: they read 0.  The offset is
+    // kept a full register value so no part of it is folded into the
+    // instruction's unsigned offset field.
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(rel_g, sgpr_u32(t < ntiles ? rel_bytes : 0u));
+    const uint32_t wsh = (uint32_t)bias_w0(kt) * SZ;
+#pragma unroll
+    for (int m = 0; m < C::BLD; ++m) {
+      uint32_t off = b_off[m] + wsh;
+      asm volatile("" : "+v"(off));
+      tb.b[m] = bload128(rr, off);
+    }
+  };
 
   f32x4 acc[D / 16];
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{};
-  float m_run = kNegInf, l_run = 0.f;
-  // One LDS tile per wave, [key][VSP]; 16 lanes write one 256-byte row.
-  // It is rewritten only after the previous tile's reads (same wave, LDS
-  // ops in order), so the register copy in vreg is the only V prefetch.
-  T* Vs = reinterpret_cast<T*>(smem) + wave * NK * VSP;
+  // Softmax reference: the column max of the split's first tile (the four
+  // lanes of a column agree on it).  Later logits may exceed it; P = exp(x -
+  // m_ref) stays finite as long as they exceed it by less than kOver, which
+  // a running check confirms.  If not, the split is streamed a second time
+  // with m_ref = the split's true column max (then no P exceeds 1).
+  float m_ref = kNegInf, l_run = 0.f;
+  float m_all = kNegInf;        // running max of this lane's logits
+  bool second_pass = false;     // wave-uniform
+  uint64_t over = 0;            // lanes that saw x > m_ref + kOver
 
-  for (int seg = t_begin; seg < t_end; seg += kSegTiles) {
-    const int seg_end = imin(t_end, seg + kSegTiles);
-    // Page ids of the segment: register r, lane i holds page pg_base+64r+i.
-    const int pg_base = (s_lo >> 4) + 2 * seg;
-    int pid[4];
+  auto compute = [&](const Tile<T, D>& tb, int t) {
+    const int kt = s_lo + t * NK;
+    // The tile's K rows, V rows and bias chunks into LDS (after the
+    // previous tile's reads of them: one wave's LDS accesses run in order).
+    wave_lds_fence();
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      pid[r] = iclamp((int)bload32(bt_rsrc, (uint32_t)(pg_base + 64 * r + lane) * 4u), 0,
-                      P.num_blocks - 1);
-    auto page_rsrc = [&](const char* base, int seq_page) {
-      const int p = iclamp(seq_page - pg_base, 0, 255);   // wave-uniform
-      const int r = p >> 6;
-      const int v = r == 0 ? pid[0] : r == 1 ? pid[1] : r == 2 ? pid[2] : pid[3];
-      const int64_t page = __builtin_amdgcn_readlane(v, p & 63);
-      return make_rsrc(base + page * page_bytes, page_bytes);
-    };
-
-    // K operands and raw bias of tile t; every lane loads unconditionally
-    // (kOOB for keys outside the split and for t >= seg_end).
-    auto load_k = [&](KBuf<T, D>& buf, int t) {
-      const int kt = s_lo + t * NK;                   // multiple of 16
-      const bool tile_ok = t < seg_end;
-      const __amdgpu_buffer_rsrc_t r0 = page_rsrc(kg, kt >> 4);
-      const __amdgpu_buffer_rsrc_t r1 = page_rsrc(kg, (kt >> 4) + 1);
+    for (int i = 0; i < C::VLD; ++i) {
+      const int key = KPL * i + lane / CPR, chunk = (lane % CPR) * VEC;
+      *reinterpret_cast<uint4*>(Ks + key * C::KP + chunk) = tb.k[i];
+      *reinterpret_cast<uint4*>(Vs + key * VSP + chunk) = tb.v[i];
+    }
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        const int j = kt + 16 * blk + col;
-        const bool ok = tile_ok && j >= v_lo && j < s_hi;
-        const uint32_t off = ok ? (uint32_t)(j & 15) * slot_bytes + head_bytes : kOOB;
-        if constexpr (C::kBF16) {
+    for (int m = 0; m < C::BLD; ++m) {
+      const int idx = m * 64 + lane;
+      *reinterpret_cast<uint4*>(Bs + (idx / C::BCH) * C::BW + (idx % C::BCH) * VEC) = tb.b[m];
+    }
+    wave_lds_fence();
+    // S^T blocks: lane holds head col, keys kt + 16 blk + 4 u4 + i.  A
+    // operand: key 16 blk + col, d = 32 st + 8 u4 .. (bf16) or 4 st + u4.
+    f32x4 s[2];
 #pragma unroll
-          for (int st = 0; st < C::KSTEPS; ++st)
-            buf.k[blk][st] = __builtin_bit_cast(
-                bf16x8, bload128(blk ? r1 : r0, off + (uint32_t)(32 * st + 8 * u4) * SZ));
-        } else {
+    for (int blk = 0; blk < 2; ++blk) {
+      s[blk] = f32x4{};
+      const T* kr = Ks + (16 * blk + col) * C::KP;
 #pragma unroll
-          for (int st = 0; st < C::KSTEPS; ++st)
-            buf.k[blk][st] = __builtin_bit_cast(
-                float, bload32(blk ? r1 : r0, off + (uint32_t)(4 * st + u4) * SZ));
-        }
+      for (int st = 0; st < C::KSTEPS; ++st) {
+        if constexpr (C::kBF16)
+          s[blk] = mfma16(*reinterpret_cast<const bf16x8*>(kr + 32 * st + 8 * u4), qop[st], s[blk]);
+        else
+          s[blk] = mfma16(kr[4 * st + u4], qop[st], s[blk]);
       }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int j = kt + 16 * (i >> 2) + 4 * u4 + (i & 3);
-        const bool vis = tile_ok && cval && j >= v_lo && j < s_hi;
-        const uint32_t off = vis ? (uint32_t)(col * R + imin(pq - j, R - 1)) * SZ : kOOB;
-        buf.bias[i] = C::kBF16 ? bload16(rel_rsrc, off) : bload32(rel_rsrc, off);
-      }
-    };
-
-    // V rows of tile t: load i covers keys (i*64)/CPR .. +64/CPR, all in
-    // page block (i*64/CPR) >> 4 of the tile.
-    uint4 vreg[C::VLOADS];
-    auto load_v = [&](int t) {
-      const int kt = s_lo + t * NK;
-      const bool tile_ok = t < seg_end;
-      const __amdgpu_buffer_rsrc_t r0 = page_rsrc(vg, kt >> 4);
-      const __amdgpu_buffer_rsrc_t r1 = page_rsrc(vg, (kt >> 4) + 1);
-#pragma unroll
-      for (int i = 0; i < C::VLOADS; ++i) {
-        const int idx = i * 64 + lane;
-        const int key = idx / CPR, ch = idx % CPR;
-        const int j = kt + key;
-        const bool ok = tile_ok && j >= v_lo && j < s_hi;
-        const uint32_t off =
-            ok ? (uint32_t)(j & 15) * slot_bytes + head_bytes + (uint32_t)ch * 16u : kOOB;
-        vreg[i] = bload128(((i * 64 / CPR) >> 4) ? r1 : r0, off);
-      }
-    };
-    auto store_v = [&]() {
-#pragma unroll
-      for (int i = 0; i < C::VLOADS; ++i) {
-        const int idx = i * 64 + lane;
-        const int key = idx / CPR, ch = idx % CPR;
-        *reinterpret_cast<uint4*>(Vs + key * VSP + ch * VEC) = vreg[i];
-      }
-    };
-
-    auto compute_tile = [&](const KBuf<T, D>& buf, int t) {
-      const int kt = s_lo + t * NK;
-      // S^T blocks: lane holds head `col`, keys kt + 16*blk + 4*u4 + i.
-      f32x4 s[2];
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        s[blk] = f32x4{};
-#pragma unroll
-        for (int st = 0; st < C::KSTEPS; ++st) s[blk] = mfma16(buf.k[blk][st], qop[st], s[blk]);
-      }
-      float x[8];
-      float mx = kNegInf;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int j = kt + 16 * (i >> 2) + 4 * u4 + (i & 3);
-        const bool vis = cval && j >= v_lo && j < s_hi;
-        x[i] = vis ? fmaf(s[i >> 2][i & 3], P.scale, raw_to_f32<T>(buf.bias[i])) : kNegInf;
-        mx = fmaxf(mx, x[i]);
-      }
-      mx = fmaxf(mx, xor_lane(mx, 16));
-      mx = fmaxf(mx, xor_lane(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = fast_exp2((m_run - m_use) * kLog2e);
-      m_run = m_new;
-      const float mb = m_use * kLog2e;
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) acc[dt] *= alpha;
-      float lsum = 0.f;
-      if constexpr (C::kBF16) {
-        bf16x8 pb;
+    }
+    // Bias of key c = 16 blk + i (i < 4) of the lane: distance pq - kt -
+    // 4 u4 - c, entry (distance - w0) of the head's staged run.
+    float bias[8];
+    {
+      const T* br = Bs + col * C::BW;
+      const int e3 = pq - kt - 4 * u4 - 3 - bias_w0(kt);   // entry of c = 3
+      if constexpr (CLAMP) {
+        const int w0 = bias_w0(kt);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const bf16 r = from_f32<bf16>(fast_exp2(fmaf(x[i], kLog2e, -mb)));
-          pb[i] = r;
-          lsum += to_f32(r);
+          const int d = pq - kt - 4 * u4 - (16 * (i >> 2) + (i & 3));
+          bias[i] = to_f32(br[iclamp(imin(d, R - 1) - w0, 0, C::BW - 1)]);
         }
-        // V^T operand: contraction slots (u4, e) hold keys 4*u4 + e (e < 4)
-        // and 16 + 4*u4 + e - 4 (e >= 4), the keys of pb's slots.
+      } else if constexpr (C::kBF16) {
+        // Four consecutive entries per block: c = 3, 2, 1, 0 upwards.
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+          const int e = iclamp(e3 - 16 * blk, 0, C::BW - 4);
+          uint2 r;
+          __builtin_memcpy(&r, br + e, 8);
+          bias[4 * blk + 3] = __builtin_bit_cast(float, r.x << 16);
+          bias[4 * blk + 2] = __builtin_bit_cast(float, r.x & 0xffff0000u);
+          bias[4 * blk + 1] = __builtin_bit_cast(float, r.y << 16);
+          bias[4 * blk + 0] = __builtin_bit_cast(float, r.y & 0xffff0000u);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          bias[i] = to_f32(br[iclamp(e3 + 3 - (16 * (i >> 2) + (i & 3)), 0, C::BW - 1)]);
+      }
+    }
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = fmaf(s[i >> 2][i & 3], P.scale, bias[i]);
+    if (kt < v_lo || kt + NK > s_hi) {                   // wave-uniform: edge tile
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int j = kt + 16 * (i >> 2) + 4 * u4 + (i & 3);
+        x[i] = (j >= v_lo && j < s_hi) ? x[i] : kNegInf;
+      }
+    }
+    float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                     fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    // P = exp(x - m_ref) rounded to the input type, row sums from the
+    // rounded values, and O^T += V^T . P^T.
+    auto pv = [&](const float (&xv)[8]) {
+      const float mb = m_ref == kNegInf ? 0.f : m_ref * kLog2e;
+      if constexpr (C::kBF16) {
+        bf16x8 pb;
+        const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+          const bf16x2 pr = {from_f32<bf16>(fast_exp2(fmaf(xv[i], kLog2e, -mb))),
+                             from_f32<bf16>(fast_exp2(fmaf(xv[i + 1], kLog2e, -mb)))};
+          pb[i] = pr[0];
+          pb[i + 1] = pr[1];
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
+        }
+        // V^T operand: contraction slots (u4, e) hold keys 4 u4 + e (e < 4)
+        // and 16 + 4 u4 + e - 4 (e >= 4), the keys of pb's slots.  A
+        // transposed read: lane jj of a 16-lane group points at key
+        // 4 u4 + jj / 4, columns 4 (jj % 4) .. +3; lane i receives column i
+        // of those four keys.
         const int jj = lane & 15;
         const T* r0 = Vs + (4 * u4 + (jj >> 2)) * VSP + 4 * (jj & 3);
         const T* r1 = r0 + 16 * VSP;
@@ -270,7 +360,6 @@ decode_kernel(const DecodeParams P) {
               (__attribute__((address_space(3))) i16x4*)(r0 + 16 * dt));
           const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (__attribute__((address_space(3))) i16x4*)(r1 + 16 * dt));
-          typedef short i16x8 __attribute__((ext_vector_type(8)));
           const i16x8 a16 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           acc[dt] = mfma16(__builtin_bit_cast(bf16x8, a16), pb, acc[dt]);
         }
@@ -278,8 +367,8 @@ decode_kernel(const DecodeParams P) {
         float pf[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          pf[i] = fast_exp2(fmaf(x[i], kLog2e, -mb));
-          lsum += pf[i];
+          pf[i] = fast_exp2(fmaf(xv[i], kLog2e, -mb));
+          l_run += pf[i];
         }
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) {
@@ -289,92 +378,74 @@ decode_kernel(const DecodeParams P) {
             acc[dt] = mfma16(vc[(16 * (i >> 2) + 4 * u4 + (i & 3)) * VSP], pf[i], acc[dt]);
         }
       }
-      l_run = l_run * alpha + lsum;
     };
-
-    // Software pipeline, prefetch distance one tile for K, bias and V:
-    //   iteration t: issue K/bias of t+1; compute t from its K registers and
-    //   the LDS V tile; then store V of t+1 (loaded one iteration earlier)
-    //   to the LDS tile and issue V of t+2.  Loads past the end are kOOB
-    //   no-ops, so the loop body has no loads under control flow.  LDS ops of
-    //   one wave run in order; the wave barriers only keep the compiler from
-    //   moving LDS accesses across the hand-over.
-    auto lds_handover = [&]() {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    };
-    KBuf<T, D> kA, kB;
-    load_k(kA, seg);
-    load_v(seg);
-    store_v();
-    load_v(seg + 1);
-    lds_handover();
-    for (int t = seg; t < seg_end; t += 2) {
-      load_k(kB, t + 1);
-      compute_tile(kA, t);
-      if (t + 1 >= seg_end) break;
-      lds_handover();
-      store_v();
-      load_v(t + 2);
-      lds_handover();
-      load_k(kA, t + 2);
-      compute_tile(kB, t + 1);
-      if (t + 2 >= seg_end) break;
-      lds_handover();
-      store_v();
-      load_v(t + 3);
-      lds_handover();
+    if (t == 0 && !second_pass) {                        // wave-uniform
+      float m = fmaxf(mx, xor_lane(mx, 16));
+      m_ref = fmaxf(m, xor_lane(m, 32));
     }
-    lds_handover();
-  }
+    m_all = fmaxf(m_all, mx);
+    over |= __builtin_amdgcn_ballot_w64(mx > m_ref + kOver);
+    pv(x);
+  };
 
-  // Merge the four waves' states.
+  wave_lds_fence();                                      // page ids visible
+  // Ring of NBUF tile buffers: tile t computes from buffer t % NBUF while
+  // tiles t+1 .. t+DEPTH are in flight.  Loads past the last tile read
+  // nothing (zero-size descriptors), so no load sits under control flow.
+  Tile<T, D> tb[NBUF];
+  while (true) {
+#pragma unroll
+    for (int i = 0; i < DEPTH; ++i) issue(tb[i], i);
+    for (int t0 = 0;; t0 += NBUF) {
+#pragma unroll
+      for (int r = 0; r < NBUF; ++r) {
+        issue(tb[(r + DEPTH) % NBUF], t0 + r + DEPTH);
+        compute(tb[r], t0 + r);
+        if (t0 + r + 1 >= ntiles) goto done;
+      }
+    }
+  done:
+    // Loads past the last tile may still be outstanding; draining them here
+    // keeps the compiler's load accounting exact for a second pass.
+    __builtin_amdgcn_s_waitcnt(0);
+    if (second_pass || over == 0) break;
+    // Rare: some logit exceeded the first tile's max by more than kOver.
+    second_pass = true;
+    const float m = fmaxf(m_all, xor_lane(m_all, 16));
+    m_ref = fmaxf(m, xor_lane(m, 32));
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{};
+    l_run = 0.f;
+  }
   l_run += xor_lane(l_run, 16);
   l_run += xor_lane(l_run, 32);
-  __syncthreads();
-  float* ored = reinterpret_cast<float*>(smem);         // [wave][col][D]
-  float* mred = ored + kDecodeWaves * 16 * D;           // [wave][col]
-  float* lred = mred + kDecodeWaves * 16;
+  if (!cval) return;
+  // acc[dt][i] = O[head col][d = 16 dt + 4 u4 + i] (unnormalised).
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  if (!multi) {
+    T* dst = static_cast<T*>(P.out) + row * D + 4 * u4;
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      ored[(wave * 16 + col) * D + 16 * dt + 4 * u4 + i] = acc[dt][i];
-  if (u4 == 0) {
-    mred[wave * 16 + col] = m_run;
-    lred[wave * 16 + col] = l_run;
-  }
-  __syncthreads();
-  for (int idx = tid; idx < G * D; idx += blockDim.x) {
-    const int c = idx / D, d = idx - c * D;
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, mred[w * 16 + c]);
-    float o = 0.f, lse = kNegInf;
-    if (M != kNegInf) {
-      float num = 0.f, den = 0.f;
-#pragma unroll
-      for (int w = 0; w < kDecodeWaves; ++w) {
-        const float sc = expf(mred[w * 16 + c] - M);
-        num += sc * ored[(w * 16 + c) * D + d];
-        den += sc * lred[w * 16 + c];
+    for (int dt = 0; dt < D / 16; ++dt) {
+      if constexpr (C::kBF16) {
+        const bf16x4 v = {from_f32<bf16>(acc[dt][0] * inv), from_f32<bf16>(acc[dt][1] * inv),
+                          from_f32<bf16>(acc[dt][2] * inv), from_f32<bf16>(acc[dt][3] * inv)};
+        *reinterpret_cast<bf16x4*>(dst + 16 * dt) = v;
+      } else {
+        *reinterpret_cast<f32x4*>(dst + 16 * dt) = acc[dt] * inv;
       }
-      o = num / den;
-      lse = M + logf(den);
     }
-    const int64_t row = (int64_t)b * hq + g * G + c;
-    if (P.num_splits == 1) {
-      static_cast<T*>(P.out)[row * D + d] = from_f32<T>(o);
-    } else {
-      const int64_t prow = (int64_t)split * P.num_seqs * hq + row;
-      P.part_o[prow * D + d] = o;
-      if (d == 0) P.part_lse[prow] = lse;
-    }
+  } else {
+    const int64_t prow = (int64_t)split * P.num_seqs * P.hq + row;
+    float* po = P.part_o + prow * D + 4 * u4;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt) = acc[dt] * inv;
+    if (u4 == 0)
+      P.part_lse[prow] = l_run > 0.f ? m_ref + __logf(l_run) : kNegInf;
   }
 }
 
-// One wave per (sequence, head) row; lane covers d = lane + 64 * k.
+// One wave per (sequence, head) row; lane covers d = lane + 64 * k.  Splits
+// with lse = -inf (empty) are skipped; the order of the sum is fixed.
 template <typename T, int D>
 __global__ void __launch_bounds__(256)
 combine_kernel(const CombineParams P) {
@@ -407,30 +478,47 @@ combine_kernel(const CombineParams P) {
 }
 
 template <typename T, int D>
-hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
+size_t decode_lds_t(const DecodeParams& p) {
+  return Decode<T, D>::fixed_lds() + (size_t)p.pid_cap * 4;
+}
+
+template <typename T, int D, bool CLAMP>
+hipError_t launch_decode_c(const DecodeParams& p, hipStream_t stream) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<T, D>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)Decode<T, D>::lds_bytes());
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&decode_kernel<T, D, CLAMP>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const dim3 grid(p.hkv, p.num_splits, p.num_seqs);
-  decode_kernel<T, D><<<grid, dim3(64 * kDecodeWaves), Decode<T, D>::lds_bytes(), stream>>>(p);
+  decode_kernel<T, D, CLAMP><<<grid, dim3(64), decode_lds_t<T, D>(p), stream>>>(p);
   return hipGetLastError();
 }
 
 template <typename T, int D>
+hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
+  return p.clamp ? launch_decode_c<T, D, true>(p, stream)
+                 : launch_decode_c<T, D, false>(p, stream);
+}
+
+template <typename T, int D>
 hipError_t launch_combine_t(const CombineParams& p, hipStream_t stream) {
-  combine_kernel<T, D><<<dim3((p.rows + 3) / 4), dim3(256), 0, stream>>>(p);
+  const unsigned blocks = (unsigned)((p.rows + 3) / 4);
+  combine_kernel<T, D><<<dim3(blocks), dim3(256), 0, stream>>>(p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim,
-                         hipStream_t stream) {
+size_t decode_lds_bytes(const DecodeParams& p, int dtype, int head_dim) {
+  if (dtype == 0)
+    return head_dim == 64 ? decode_lds_t<bf16, 64>(p) : decode_lds_t<bf16, 128>(p);
+  return head_dim == 64 ? decode_lds_t<float, 64>(p) : decode_lds_t<float, 128>(p);
+}
+
+hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, hipStream_t stream) {
   if (dtype == 0)
     return head_dim == 64 ? launch_decode_t<bf16, 64>(p, stream)
                           : launch_decode_t<bf16, 128>(p, stream);
@@ -438,8 +526,7 @@ hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim,
                         : launch_decode_t<float, 128>(p, stream);
 }
 
-hipError_t launch_combine(const CombineParams& p, int dtype, int head_dim,
-                          hipStream_t stream) {
+hipError_t launch_combine(const CombineParams& p, int dtype, int head_dim, hipStream_t stream) {
   if (dtype == 0)
     return head_dim == 64 ? launch_combine_t<bf16, 64>(p, stream)
                           : launch_combine_t<bf16, 128>(p, stream);

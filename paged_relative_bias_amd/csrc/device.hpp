@@ -80,6 +80,13 @@ __device__ __forceinline__ uint32_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t o
   return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
 }
 
+// A wave-uniform value forced into an SGPR (buffer descriptors must be
+// scalar; a uniform value the compiler computed with VALU ops would
+// otherwise make it emit a waterfall loop around each buffer access).
+__device__ __forceinline__ uint32_t sgpr_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)x);
+}
+
 __device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
 __device__ __forceinline__ int imax(int a, int b) { return a > b ? a : b; }
 __device__ __forceinline__ int iclamp(int x, int lo, int hi) {

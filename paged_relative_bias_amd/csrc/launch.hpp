@@ -13,7 +13,8 @@ constexpr int kPrefillKeys = 32;
 // floor(128 / G) query tokens.
 constexpr int kPrefillWaves = 4;
 constexpr int kDecodeKeys = 32;
-constexpr int kDecodeWaves = 4;
+// Decode waves per compute unit the split heuristic aims for (one per SIMD).
+constexpr int kDecodeWavesPerCU = 4;
 constexpr int kMaxSplits = 128;
 constexpr int kMaxGroup = 16;
 
@@ -49,6 +50,10 @@ struct DecodeParams {
   float* part_lse;    // [splits, B, Hq]
   int32_t num_seqs, hq, hkv, group;
   int32_t num_blocks, max_blocks, rel_len, window, num_splits;
+  int32_t chunk_tiles;  // 32-key tiles per split
+  int32_t pid_cap;      // entries of the per-wave page-id table (>= 2 * chunk_tiles + 16)
+  int32_t max_seq_len;  // host bound on seq_lens
+  int32_t clamp;        // 1: a visible distance may exceed rel_len - 1
   float scale;
 };
 
@@ -65,6 +70,7 @@ hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim, hipSt
 size_t prefill_lds_bytes(int dtype, int head_dim, int waves, int sb_pitch, int pid_cap);
 hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim,
                          hipStream_t stream);
+size_t decode_lds_bytes(const DecodeParams& p, int dtype, int head_dim);
 hipError_t launch_combine(const CombineParams& p, int dtype, int head_dim,
                           hipStream_t stream);
 

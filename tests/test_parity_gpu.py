@@ -152,6 +152,38 @@ def test_decode_matches_oracle(case):
         U.compare(out, ref, dtype, f"{name}/s{s}")
 
 
+def _bias_spike(b, dist, amount):
+    """Adds `amount` to the bias at one distance (every row and head): the
+    logits of one key per row jump far above the others."""
+    rel = b.rel_logits.clone()
+    rel[:, :, dist] = (rel[:, :, dist].float() + amount).to(rel.dtype)
+    return dataclasses.replace(b, rel_logits=rel)
+
+
+@pytest.mark.parametrize("dist,amount", [(0, 60.0), (0, 30.0), ("far", 60.0)])
+def test_decode_logit_spike(dist, amount):
+    """A logit far above the first tile's (distance 0 sits in the last tile)
+    or far below the rest (the farthest key carries the spike): the softmax
+    reference must follow without overflow or loss."""
+    b = _mk(42, [2000, 700, 3000], [1, 1, 1], Hq=12, Hkv=4, W=0, R=4096)
+    d_ = 600 if dist == "far" else dist
+    b = _bias_spike(b, d_, amount)
+    ref, _ = oracle.run_batch(b)
+    d = U.Dev(b)
+    for s in (1, 3):
+        _say(f"decode spike dist={dist} amount={amount} splits={s}")
+        U.compare(U.decode(d, splits=s), ref, "bf16", f"spike/{dist}/{amount}/s{s}")
+
+
+@pytest.mark.parametrize("dist,amount", [(0, 60.0), (300, 60.0)])
+def test_prefill_logit_spike(dist, amount):
+    b = _mk(43, [700, 450], [700, 200], Hq=12, Hkv=4, W=0, R=1024)
+    b = _bias_spike(b, dist, amount)
+    _say(f"prefill spike dist={dist} amount={amount}")
+    ref, _ = oracle.run_batch(b)
+    U.compare(U.prefill(U.Dev(b)), ref, "bf16", f"prefill_spike/{dist}/{amount}")
+
+
 def test_decode_equals_last_prefill_row():
     b = _mk(40, [700, 900], [150, 64], Hq=12, Hkv=4, W=512, R=512)
     _say("decode vs last prefill row")
