@@ -48,9 +48,9 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// Lazy rescaling threshold, in log2 units: P may reach 2^kLazy.
-constexpr float kLazy = 8.f;
-constexpr float kLn2 = 0.6931471805599453f;
+// Largest logit excess over the reference (natural units) for which P =
+// exp(x - m_ref) and the running sums stay far from fp32 / bf16 overflow.
+constexpr float kOver = 40.f;
 
 template <typename T, int D>
 struct Prefill {
@@ -61,10 +61,10 @@ struct Prefill {
   static constexpr int KP = D + VEC;                     // K row pitch
   static constexpr int VP = kBF16 ? D + 16 : D + 4;      // V row pitch
   static constexpr int QSTEPS = kBF16 ? D / 16 : D / 2;  // MFMA k-steps over D
-  static constexpr int TILE_INST = 2 * N * CPR / 64;     // K+V wave loads per tile
-  static constexpr int HALF_INST = TILE_INST / 2;
   static constexpr int KPI = 64 / CPR;                   // keys per wave load
-  static constexpr int KV_PER = (TILE_INST + kPrefillWaves - 1) / kPrefillWaves;
+  static constexpr int KW = N / kPrefillWaves;           // keys each wave loads
+  static constexpr int LPT = KW / KPI;                   // its loads per tensor
+  static constexpr int KV_PER = 2 * LPT;                 // K then V
   static constexpr int SBC_MAX = (N + VEC) / VEC;        // bias chunks per row
   static constexpr int BIAS_PER = (32 * SBC_MAX + 63) / 64;
   using QOp = typename std::conditional<kBF16, bf16x8, float>::type;
@@ -149,6 +149,7 @@ prefill_kernel(const PrefillParams P) {
   unsigned char* bias_lds = smem + 2 * C::stage_bytes();
   const int sbp = P.sb_pitch;
   int* pid_lds = reinterpret_cast<int*>(bias_lds + (size_t)nw * 2 * 32 * sbp);
+  int* ovf_lds = pid_lds + P.pid_cap;                    // one flag per wave
 
   // Page ids of keys [jb, je).
   const int pg_lo = jb >> 4;
@@ -193,18 +194,15 @@ prefill_kernel(const PrefillParams P) {
     uint4 kv[C::KV_PER];
     uint4 b[C::BIAS_PER];
   };
-  // Lane constants of the loads (independent of the tile).  K/V load i of
-  // this wave: keys kk_i .. kk_i + KPI of the tile, lane -> key kk_i +
-  // lane / CPR, 16-byte chunk lane % CPR; tiles start at multiples of 16,
-  // so the slot of the key inside its page is fixed.
-  uint32_t kv_lane[C::KV_PER];
+  // Lane constants of the loads (independent of the tile).  Wave w loads
+  // keys KW*w .. KW*w + KW - 1 of the tile (one page: tiles start at
+  // multiples of 16); its load i of K (and of V) covers keys KW*w + KPI*i +
+  // lane / CPR, 16-byte chunk lane % CPR.
+  uint32_t kv_lane[C::LPT];
 #pragma unroll
-  for (int i = 0; i < C::KV_PER; ++i) {
-    const int k = wave + nw * i;
-    const int kk = (k >= C::HALF_INST ? k - C::HALF_INST : k) * KPI;
-    kv_lane[i] = (uint32_t)((kk + lane / CPR) & 15) * slot_bytes + head_bytes +
-                 (uint32_t)(lane % CPR) * 16u;
-  }
+  for (int i = 0; i < C::LPT; ++i)
+    kv_lane[i] = (uint32_t)((C::KW * wave + KPI * i + lane / CPR) & 15) * slot_bytes +
+                 head_bytes + (uint32_t)(lane % CPR) * 16u;
   // Bias load i: row r = c / sbc (token rt, head rh), chunk c % sbc.
   uint32_t b_row[C::BIAS_PER];   // row offset | 0x80000000 if the row is unused
   int b_pos[C::BIAS_PER];        // position of the row's token + (part * VEC << 20)
@@ -219,21 +217,23 @@ prefill_kernel(const PrefillParams P) {
                (ok ? 0u : kOOB);
     b_pos[i] = pbase + rt;
   }
-  // Loads of tile kt.  Keys outside [jb, je) and rows the wave does not
-  // stage read as kOOB (zero, no memory traffic); no control flow.
+  // Loads of tile kt.  The K/V descriptors of the wave's page end at key
+  // je (keys past it, and whole tiles past the last, read zero without
+  // traffic); keys before jb are real cache rows.  Rows the wave does not
+  // stage read as kOOB.  No control flow around any load.
   auto issue = [&](Regs& rg, int kt) {
+    {
+      const int key0 = kt + C::KW * wave;                 // wave-uniform
+      const int pgi = iclamp((key0 >> 4) - pg_lo, 0, P.pid_cap - 1);
+      const uint64_t page = (uint32_t)__builtin_amdgcn_readfirstlane(pid_lds[pgi]);
+      const uint32_t nrec = sgpr_u32((uint32_t)iclamp(je - (key0 & ~15), 0, 16) * slot_bytes);
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + page * page_bytes, nrec);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + page * page_bytes, nrec);
 #pragma unroll
-    for (int i = 0; i < C::KV_PER; ++i) {
-      const int k = wave + nw * i;                        // wave-uniform
-      const bool is_v = k >= C::HALF_INST;
-      const int kk = (is_v ? k - C::HALF_INST : k) * KPI;
-      const int blk = iclamp(((kt + kk) >> 4) - pg_lo, 0, P.pid_cap - 1);
-      const int64_t page = __builtin_amdgcn_readfirstlane(pid_lds[blk]);
-      const __amdgpu_buffer_rsrc_t r =
-          make_rsrc((is_v ? vg : kg) + page * page_bytes, page_bytes);
-      const int j = kt + kk + lane / CPR;
-      const bool ok = k < C::TILE_INST && (uint32_t)(j - jb) < (uint32_t)(je - jb);
-      rg.kv[i] = bload128(r, kv_lane[i] | (ok ? 0u : kOOB));
+      for (int i = 0; i < C::LPT; ++i) {
+        rg.kv[i] = bload128(rk, kv_lane[i]);
+        rg.kv[C::LPT + i] = bload128(rv, kv_lane[i]);
+      }
     }
     const bool wtile = wact && kt < wje && kt + N > wjb;  // wave-uniform
 #pragma unroll
@@ -249,18 +249,11 @@ prefill_kernel(const PrefillParams P) {
     T* Ks = stage(st);
     T* Vs = Ks + N * KP;
 #pragma unroll
-    for (int i = 0; i < C::KV_PER; ++i) {
-      const int k = wave + nw * i;
-      if (k < C::TILE_INST) {                             // wave-uniform
-        const bool is_v = k >= C::HALF_INST;
-        const int key = (is_v ? k - C::HALF_INST : k) * KPI + lane / CPR;
-        const int part = lane % CPR;
-        if (is_v) {
-          *reinterpret_cast<uint4*>(Vs + key * VP + part * VEC) = rg.kv[i];
-        } else {
-          *reinterpret_cast<uint4*>(Ks + key * KP + part * VEC) = rg.kv[i];
-        }
-      }
+    for (int i = 0; i < C::LPT; ++i) {
+      const int key = C::KW * wave + KPI * i + lane / CPR;
+      const int chunk = (lane % CPR) * VEC;
+      *reinterpret_cast<uint4*>(Ks + key * KP + chunk) = rg.kv[i];
+      *reinterpret_cast<uint4*>(Vs + key * VP + chunk) = rg.kv[C::LPT + i];
     }
     unsigned char* Bw = bias_lds + (size_t)(wave * 2 + st) * 32 * sbp;
 #pragma unroll
@@ -280,8 +273,16 @@ prefill_kernel(const PrefillParams P) {
   f32x16 acc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
-  float m_ref = kNegInf;   // reference max of the logits
+  // Softmax reference of the column: the max of its logits in the first
+  // tile where it has a visible key (the two lanes of a column agree on it).
+  // Later logits may exceed it; P = exp(x - m_ref) stays finite while they
+  // exceed it by less than kOver, which a running check confirms; if not,
+  // the workgroup streams its keys again with m_ref = the true column max.
+  float m_ref = kNegInf;
   float l_run = 0.f;
+  float m_all = kNegInf;        // running max of this lane's logits
+  bool second_pass = false;     // workgroup-uniform
+  uint64_t over = 0;            // lanes that saw x > m_ref + kOver
 
   // ---- compute one tile from LDS stage st --------------------------------
   auto compute = [&](int kt, int st) {
@@ -342,18 +343,16 @@ prefill_kernel(const PrefillParams P) {
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, x[i]);
-    mx = fmaxf(mx, xor_lane(mx, 32));
-    // Move the reference max only when this tile exceeds it by > kLazy
-    // (in log2 units), so that P <= 2^kLazy.
-    const bool move = mx > m_ref + kLazy * kLn2;
-    if (__builtin_amdgcn_ballot_w64(move)) {              // wave-uniform
-      const float m_new = move ? mx : m_ref;
-      const float alpha = move ? fast_exp2((m_ref - m_new) * kLog2e) : 1.f;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= alpha;
-      l_run *= alpha;
-      m_ref = m_new;
+    // Columns still without a reference take this tile's column max (which
+    // stays -inf while the column has no visible key: then P = 0).
+    if (!second_pass && __builtin_amdgcn_ballot_w64(m_ref == kNegInf)) {
+      const float mc = fmaxf(mx, xor_lane(mx, 32));
+      m_ref = m_ref == kNegInf ? mc : m_ref;
     }
+    m_all = fmaxf(m_all, mx);
+    // Padding columns (no such head or token) may see arbitrary staged
+    // values; only real columns decide on a second pass.
+    over |= __builtin_amdgcn_ballot_w64(cval && mx > m_ref + kOver);
     const float mb = m_ref == kNegInf ? 0.f : m_ref * kLog2e;
     if constexpr (C::kBF16) {
       bf16x8 pb[2];
@@ -409,26 +408,41 @@ prefill_kernel(const PrefillParams P) {
   // tile kt sits in an LDS stage, tile kt+N in one buffer (issued a step
   // earlier) and tile kt+2N is issued into the other.  Loads past the last
   // tile are kOOB no-ops, so no load sits under control flow.
-  lds_barrier();                                         // page ids ready
-  int kt = jb & ~15;
   Regs ra, rb;
-  issue(ra, kt);
-  issue(rb, kt + N);
-  commit(ra, 0);
-  lds_barrier();
   while (true) {
-    issue(ra, kt + 2 * N);
-    compute(kt, 0);
-    if (kt + N >= je) break;                             // workgroup-uniform
-    commit(rb, 1);
-    lds_barrier();
-    kt += N;
-    issue(rb, kt + 2 * N);
-    compute(kt, 1);
-    if (kt + N >= je) break;
+    lds_barrier();                                       // page ids ready
+    int kt = jb & ~15;
+    issue(ra, kt);
+    issue(rb, kt + N);
     commit(ra, 0);
     lds_barrier();
-    kt += N;
+    while (true) {
+      issue(ra, kt + 2 * N);
+      compute(kt, 0);
+      if (kt + N >= je) break;                           // workgroup-uniform
+      commit(rb, 1);
+      lds_barrier();
+      kt += N;
+      issue(rb, kt + 2 * N);
+      compute(kt, 1);
+      if (kt + N >= je) break;
+      commit(ra, 0);
+      lds_barrier();
+      kt += N;
+    }
+    // Prefetches past the last tile may be outstanding: drain them, and
+    // decide workgroup-wide whether a second pass is needed.
+    __builtin_amdgcn_s_waitcnt(0);
+    if (lane == 0) ovf_lds[wave] = over != 0 ? 1 : 0;
+    lds_barrier();
+    const bool any = (ovf_lds[0] | ovf_lds[1] | ovf_lds[2] | ovf_lds[3]) != 0;
+    if (second_pass || !any) break;
+    // Rare: some logit exceeded its column's reference by more than kOver.
+    second_pass = true;
+    m_ref = fmaxf(m_all, xor_lane(m_all, 32));
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
+    l_run = 0.f;
   }
 
   if (!wact) return;
@@ -447,7 +461,7 @@ prefill_kernel(const PrefillParams P) {
 template <typename T, int D>
 size_t lds_bytes_t(int waves, int sb_pitch, int pid_cap) {
   return 2 * Prefill<T, D>::stage_bytes() + (size_t)waves * 2 * 32 * sb_pitch +
-         (size_t)pid_cap * 4;
+         (size_t)pid_cap * 4 + (size_t)kPrefillWaves * 4;
 }
 
 template <typename T, int D>
