@@ -17,9 +17,10 @@
 // Key tiles of 32 keys sweep the union of the block's visible ranges,
 // double-buffered in LDS:
 //   * K rows (row-major, 16-byte pad) and V rows (row-major, 32-byte pad)
-//     are gathered through the block table by buffer loads whose 64 lanes
-//     cover keys of one page (page id uniform per instruction); the page
-//     ids of the block's range sit in an LDS table;
+//     are gathered through the block table: each wave loads 8 keys of the
+//     tile (one page) through a buffer descriptor that ends at the block's
+//     last key (later keys, and tiles past the last, read zero without
+//     traffic); the page ids of the block's range sit in an LDS table;
 //   * every wave copies the bias runs of its 32 rows for the tile: for
 //     (token, head) the tile needs one contiguous run of the distance axis,
 //     taken from an aligned window of sb entries with 16-byte loads;
@@ -30,9 +31,12 @@
 //   S^T[key][col] = K . Q^T       32x32x16 bf16 MFMA (32x32x2 f32 for fp32)
 //   x = scale * S + bias          mask by select only on boundary tiles
 //   online softmax per column     two lanes per column (l, l ^ 32); the
-//                                 reference max moves only when the tile
-//                                 max exceeds it by more than 2^8 in the
-//                                 exponent, so rescaling is rare
+//                                 reference max is the column's max in its
+//                                 first tile with a visible key and the
+//                                 accumulators are never rescaled; a
+//                                 workgroup whose real columns see a logit
+//                                 more than kOver above it streams its keys
+//                                 a second time with the exact column max
 //   O^T[d][col] += V^T . P^T      V^T operand from ds_read_tr16_b64, P^T
 //                                 from registers; row sums of the rounded P
 //                                 with v_dot2_f32_bf16.
@@ -407,7 +411,7 @@ prefill_kernel(const PrefillParams P) {
   // Two register buffers keep two tiles in flight: at the top of each step
   // tile kt sits in an LDS stage, tile kt+N in one buffer (issued a step
   // earlier) and tile kt+2N is issued into the other.  Loads past the last
-  // tile are kOOB no-ops, so no load sits under control flow.
+  // tile read nothing, so no load sits under control flow.
   Regs ra, rb;
   while (true) {
     lds_barrier();                                       // page ids ready
