@@ -275,6 +275,18 @@ inkling_status_t inkling_rel_attn_decode(const void* q, const void* k_cache, con
   const int64_t max_vis_d = window > 0 ? (int64_t)window - 1 : (int64_t)dims->max_seq_len - 1;
   p.clamp = max_vis_d > dims->rel_len - 1 ? 1 : 0;
   const size_t esz = dtype_size(dims->dtype);
+  // As many adjacent KV heads per workgroup as divide Hkv and fit in LDS
+  // (bf16); a single head per workgroup otherwise.
+  p.heads_per_wg = 1;
+  if (dims->dtype == 0) {
+    for (int nh = kDecodeMaxHeadsPerWG; nh > 1; nh /= 2) {
+      p.heads_per_wg = nh;
+      if (dims->num_kv_heads % nh == 0 &&
+          decode_lds_bytes(p, dims->dtype, dims->head_dim) <= 160 * 1024)
+        break;
+      p.heads_per_wg = 1;
+    }
+  }
   if (decode_lds_bytes(p, dims->dtype, dims->head_dim) > 160 * 1024)
     return INKLING_ERR_UNSUPPORTED;
   // 32-bit buffer offsets: one page, and the bias rows of one KV head.

@@ -7,34 +7,43 @@
 // the split-KV decode the vLLM page describes (section "Changes": up to 128
 // splits, with a helper that picks the count).
 //
-// Work decomposition.  One wave per (KV head g, split, sequence b); the G
-// query heads of the KV head are the MFMA columns (G <= 16).  A split is a
-// run of at most `chunk_tiles` 32-key tiles of the sequence's visible keys,
-// so every wave of a launch streams about the same number of bytes whatever
-// the sequence lengths; sequence b uses ceil(tiles_b / chunk_tiles) splits
-// and the waves beyond that only mark their partial empty.
+// Work decomposition.  One workgroup per (group of NH adjacent KV heads,
+// split, sequence b) with one wave per KV head g (NH = 4, 2 or 1: the
+// largest that divides Hkv and fits in LDS; 1 for fp32).  The G query heads
+// of a KV head are its wave's MFMA columns (G <= 16).  A split is a run of
+// at most `chunk_tiles` 32-key tiles of the sequence's visible keys, so
+// every workgroup of a launch streams about the same number of bytes
+// whatever the sequence lengths; sequence b uses ceil(tiles_b /
+// chunk_tiles) splits and the workgroups beyond that only mark their
+// partials empty.
 //
 // The kernel is bound by HBM bandwidth; the loop keeps DEPTH tiles of K, V
 // and bias loads in flight in a ring of register buffers:
 //   * the page ids of the split are copied once into LDS; a tile's two page
 //     ids are one broadcast LDS read, taken to SGPRs;
+//   * the NH heads of a workgroup are adjacent in every cache slot, so one
+//     wave load covers NH * D contiguous elements of one or more slots;
+//     each wave loads 32 / NH slots of the tile for all NH heads;
 //   * every K/V load goes through a per-page buffer descriptor whose size
 //     stops at the split's last key, so keys past the end (and whole tiles
 //     past the last one) read zero without any per-lane test or traffic,
 //     and each lane's offset inside a page is a loop constant;
-//   * the bias of the tile is eight 2-byte loads, one per key of the lane
-//     (distances p - j), with out-of-range offsets for keys past the query;
-//   * K is loaded straight into MFMA A-operand registers; V rows are
-//     written to a wave-private LDS tile and read back transposed with
-//     ds_read_tr16_b64.
+//   * the bias of the tile is, per query head, an aligned run of 40
+//     entries of the distance axis loaded as 16-byte chunks (chunks left of
+//     the row start read zero through the descriptor bound);
+//   * the loads are written to an LDS stage (two stages, alternating by
+//     tile, when several waves share it; one barrier per tile), each wave
+//     reads its head's K rows as MFMA A operands and its V rows transposed
+//     with ds_read_tr16_b64.
 // Per tile: S^T[key][head] = K . Q^T (16x16x32 bf16 MFMA); x = scale * S +
 // bias; masking by select only on the first and last tile of the split;
-// online softmax whose reference max moves only when a column's logits
-// exceed it by more than 2^8 (in exp2 units), so the common tile needs no
-// cross-lane exchange; P rounded to bf16 with its row sum taken from the
-// rounded values; O^T[d][head] += V^T . P^T.  One split writes the output;
-// otherwise each wave writes its normalised partial and log-sum-exp, and
-// combine_kernel merges them in split order (no atomics).
+// softmax against a fixed reference (the column max of the split's first
+// tile) with a second pass over the split, taken by the whole workgroup, in
+// the rare case that a later logit exceeds it by more than kOver; P rounded
+// to bf16 with its row sum taken from the rounded values; O^T[d][head] +=
+// V^T . P^T.  One split writes the output; otherwise each wave writes its
+// normalised partial and log-sum-exp, and combine_kernel merges them in
+// split order (no atomics).
 #include <type_traits>
 
 #include "device.hpp"
@@ -51,16 +60,18 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // exp(x - m_ref) and the running sums stay far from fp32 / bf16 overflow.
 constexpr float kOver = 40.f;
 
-template <typename T, int D>
+template <typename T, int D, int NH>
 struct Decode {
   static constexpr bool kBF16 = sizeof(T) == 2;
   static constexpr int NK = kDecodeKeys;                 // keys per tile
   static constexpr int SZ = (int)sizeof(T);
   static constexpr int VEC = 16 / SZ;                    // elements per 16 B
-  static constexpr int CPR = D / VEC;                    // 16-byte chunks per row
-  static constexpr int KPL = 64 / CPR;                   // keys per wave load
-  static constexpr int VLD = NK / KPL;                   // K (and V) loads per tile
-  static constexpr int NVOFF = 16 / KPL;                 // distinct offsets per page
+  static constexpr int CPR = D / VEC;                    // 16-byte chunks per head row
+  static constexpr int LPS = NH * CPR;                   // lanes per slot (NH head rows)
+  static constexpr int SPI = 64 / LPS;                   // slots per wave load
+  static constexpr int SPW = NK / NH;                    // slots each wave loads per tile
+  static constexpr int VLD = SPW / SPI;                  // K (and V) loads per wave and tile
+  static_assert(LPS <= 64 && SPW % SPI == 0 && 16 % SPI == 0, "load layout");
   static constexpr int KP = D + VEC;                     // K row pitch (elements)
   static constexpr int VSP = kBF16 ? D + 16 : D + 4;     // V row pitch (elements)
   static constexpr int KSTEPS = kBF16 ? D / 32 : D / 4;  // MFMA k-steps per 16 keys
@@ -69,6 +80,9 @@ struct Decode {
   static constexpr int BLD = (kMaxGroup * BCH + 63) / 64;  // bias loads per tile
   static constexpr int DEPTH = kBF16 ? 2 : 1;            // tiles in flight
   static constexpr int NBUF = DEPTH + 1;
+  // One wave alone orders its own LDS accesses; several share a tile
+  // through two LDS stages and one barrier per tile.
+  static constexpr int STAGES = NH > 1 ? 2 : 1;
   using KOp = typename std::conditional<kBF16, bf16x8, float>::type;
   static constexpr size_t k_bytes() { return (size_t)NK * KP * SZ; }
   static constexpr size_t v_bytes() { return (size_t)NK * VSP * SZ; }
@@ -76,14 +90,16 @@ struct Decode {
   // their zeros to rows nobody reads, so the store needs no condition).
   static constexpr int BROWS = (BLD * 64 + BCH - 1) / BCH;
   static constexpr size_t b_bytes() { return (size_t)BROWS * BW * SZ; }
-  static constexpr size_t fixed_lds() { return k_bytes() + v_bytes() + b_bytes(); }
+  // Stage: K of the NH heads, V of the NH heads, then each wave's bias runs.
+  static constexpr size_t stage_bytes() { return NH * (k_bytes() + v_bytes() + b_bytes()); }
+  static constexpr size_t fixed_lds() { return STAGES * stage_bytes() + 16; }
 };
 
-// One tile's loads: K rows, V rows and the heads' bias runs, all as
-// 16-byte chunks.
-template <typename T, int D>
+// One wave's loads of a tile: its K and V slots (for all NH heads) and its
+// heads' bias runs, all as 16-byte chunks.
+template <typename T, int D, int NH>
 struct Tile {
-  using C = Decode<T, D>;
+  using C = Decode<T, D, NH>;
   uint4 k[C::VLD];
   uint4 v[C::VLD];
   uint4 b[C::BLD];
@@ -97,25 +113,35 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Workgroup barrier that orders LDS only: in-flight global loads of the
+// waves are not waited for.
+__device__ __forceinline__ void wg_lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // CLAMP: some visible distance may exceed R - 1 (window or context longer
 // than the bias), so bias offsets are clamped per element.
-template <typename T, int D, bool CLAMP>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <typename T, int D, bool CLAMP, int NH>
+__global__ void __launch_bounds__(64 * NH) __attribute__((amdgpu_waves_per_eu(1, 1)))
 decode_kernel(const DecodeParams P) {
-  using C = Decode<T, D>;
-  constexpr int NK = C::NK, VSP = C::VSP, CPR = C::CPR, VEC = C::VEC, KPL = C::KPL;
+  using C = Decode<T, D, NH>;
+  constexpr int NK = C::NK, VSP = C::VSP, CPR = C::CPR, VEC = C::VEC;
+  constexpr int LPS = C::LPS, SPI = C::SPI, SPW = C::SPW;
   constexpr int DEPTH = C::DEPTH, NBUF = C::NBUF;
   constexpr uint32_t SZ = sizeof(T);
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  // LDS: K tile [NK][KP], V tile [NK][VSP], bias runs [BROWS][BW],
-  // then the split's page-id table.
-  T* Ks = reinterpret_cast<T*>(smem);
-  T* Vs = reinterpret_cast<T*>(smem + C::k_bytes());
-  T* Bs = reinterpret_cast<T*>(smem + C::k_bytes() + C::v_bytes());
+  // LDS: STAGES x {K tiles [NH][NK][KP], V tiles [NH][NK][VSP], bias runs
+  // [NH][BROWS][BW]}, the waves' second-pass flags, then the split's
+  // page-id table.
+  int* ovf_lds = reinterpret_cast<int*>(smem + C::STAGES * C::stage_bytes());
   int* pid_lds = reinterpret_cast<int*>(smem + C::fixed_lds());
 
-  const int g = blockIdx.x, split = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = NH > 1 ? __builtin_amdgcn_readfirstlane(tid >> 6) : 0;
+  const int g0 = blockIdx.x * NH, g = g0 + wave;
+  const int split = blockIdx.y, b = blockIdx.z;
   const int col = lane & 15, u4 = lane >> 4;
   const int G = P.group, R = P.rel_len, W = P.window;
   const bool cval = col < G;
@@ -125,7 +151,7 @@ decode_kernel(const DecodeParams P) {
 
   // Keys of this split: tiles [split * CT, split * CT + ntiles) of the
   // sequence's tiles, which start at the first visible key rounded down to
-  // a page boundary.
+  // a page boundary.  All of it is uniform over the workgroup.
   const int L = iclamp(P.seq_lens[b], 0, P.max_blocks * 16);
   const int pq = L - 1;                                  // query position
   const int k_lo = W > 0 ? imax(0, L - W) : 0;           // first visible key
@@ -158,7 +184,7 @@ decode_kernel(const DecodeParams P) {
     const int seq_pages = (L + 15) >> 4;
     const __amdgpu_buffer_rsrc_t bt_rsrc =
         make_rsrc(P.block_table + (int64_t)b * P.max_blocks, (uint32_t)seq_pages * 4u);
-    for (int i = lane; i < P.pid_cap; i += 64) {
+    for (int i = tid; i < P.pid_cap; i += 64 * NH) {
       const uint32_t off = i < npg ? (uint32_t)(pg_base + i) * 4u : kOOB;
       pid_lds[i] = iclamp((int)bload32(bt_rsrc, off), 0, P.num_blocks - 1);
     }
@@ -178,19 +204,20 @@ decode_kernel(const DecodeParams P) {
     }
   }
 
-  // Loop-constant lane offsets.  A page holds 16 slots x Hkv heads x D.
+  // Loop-constant lane offsets.  A page holds 16 slots x Hkv heads x D; the
+  // NH heads of the workgroup are adjacent, so one slot of them is NH * D
+  // contiguous elements.  Wave load i covers slots wave * SPW + i * SPI +
+  // lane / LPS of the tile, head g0 + (lane % LPS) / CPR, 16-byte chunk
+  // lane % CPR.
   const uint32_t slot_bytes = (uint32_t)P.hkv * D * SZ;
   const uint32_t page_bytes = 16u * slot_bytes;
-  const uint32_t head_bytes = (uint32_t)g * D * SZ;
   const char* kg = static_cast<const char*>(P.k);
   const char* vg = static_cast<const char*>(P.v);
-  // K and V load i: keys KPL * i + lane / CPR of the tile (slot of the
-  // key's page), 16-byte chunk lane % CPR of the row.
-  uint32_t kv_off[C::NVOFF];
+  uint32_t kv_off[C::VLD];
 #pragma unroll
-  for (int j = 0; j < C::NVOFF; ++j)
-    kv_off[j] = (uint32_t)((KPL * j + lane / CPR) & 15) * slot_bytes + head_bytes +
-                (uint32_t)(lane % CPR) * 16u;
+  for (int i = 0; i < C::VLD; ++i)
+    kv_off[i] = (uint32_t)((wave * SPW + i * SPI + lane / LPS) & 15) * slot_bytes +
+                (uint32_t)g0 * D * SZ + (uint32_t)(lane % LPS) * 16u;
   // Bias: for a tile at kt the keys' distances pq - kt - 31 .. pq - kt lie
   // in an aligned window [w0, w0 + BW) of each head's row; bias load m
   // brings chunk (m * 64 + lane) % BCH of head (m * 64 + lane) / BCH.
@@ -210,7 +237,9 @@ decode_kernel(const DecodeParams P) {
     return CLAMP ? imin(w, floor_to(R - NK, VEC)) : w;
   };
 
-  auto issue = [&](Tile<T, D>& tb, int t) {
+  // Loads of tile t: K rows and bias runs (kb), V rows (vv).  Both flags
+  // are constants at every call.
+  auto issue = [&](Tile<T, D, NH>& tb, int t, bool kb, bool vv) {
     const int kt = s_lo + t * NK;
     const int2 pp = *reinterpret_cast<const int2*>(pid_lds + 2 * t);
     // Descriptor fields must be scalar: readfirstlane keeps every value
@@ -223,12 +252,18 @@ decode_kernel(const DecodeParams P) {
     const __amdgpu_buffer_rsrc_t k1 = make_rsrc(kg + p1 * page_bytes, n1);
     const __amdgpu_buffer_rsrc_t v0 = make_rsrc(vg + p0 * page_bytes, n0);
     const __amdgpu_buffer_rsrc_t v1 = make_rsrc(vg + p1 * page_bytes, n1);
+    // Load i reads page (wave * SPW + i * SPI) / 16 of the tile (uniform).
+    if (kb) {
 #pragma unroll
-    for (int i = 0; i < C::VLD; ++i)
-      tb.k[i] = bload128((KPL * i) >= 16 ? k1 : k0, kv_off[i % C::NVOFF]);
+      for (int i = 0; i < C::VLD; ++i)
+        tb.k[i] = bload128(((wave * SPW + i * SPI) >> 4) ? k1 : k0, kv_off[i]);
+    }
+    if (vv) {
 #pragma unroll
-    for (int i = 0; i < C::VLD; ++i)
-      tb.v[i] = bload128((KPL * i) >= 16 ? v1 : v0, kv_off[i % C::NVOFF]);
+      for (int i = 0; i < C::VLD; ++i)
+        tb.v[i] = bload128(((wave * SPW + i * SPI) >> 4) ? v1 : v0, kv_off[i]);
+    }
+    if (!kb) return;
     // Chunks left of a row start (window of the last tile) get a negative
     // offset, out of range as an unsigned value: they read 0.  The offset is
     // kept a full register value so no part of it is folded into the
@@ -243,36 +278,49 @@ decode_kernel(const DecodeParams P) {
     }
   };
 
-  f32x4 acc[D / 16];
-#pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{};
-  // Softmax reference: the column max of the split's first tile (the four
-  // lanes of a column agree on it).  Later logits may exceed it; P = exp(x -
-  // m_ref) stays finite as long as they exceed it by less than kOver, which
-  // a running check confirms.  If not, the split is streamed a second time
-  // with m_ref = the split's true column max (then no P exceeds 1).
-  float m_ref = kNegInf, l_run = 0.f;
-  float m_all = kNegInf;        // running max of this lane's logits
-  bool second_pass = false;     // wave-uniform
-  uint64_t over = 0;            // lanes that saw x > m_ref + kOver
-
-  auto compute = [&](const Tile<T, D>& tb, int t) {
-    const int kt = s_lo + t * NK;
-    // The tile's K rows, V rows and bias chunks into LDS (after the
-    // previous tile's reads of them: one wave's LDS accesses run in order).
-    wave_lds_fence();
+  // The wave's loads of a tile into LDS stage st: its K and V slots of all
+  // NH heads, and its own bias runs.
+  auto stage_tile = [&](const Tile<T, D, NH>& tb, int st) {
+    unsigned char* base = smem + (size_t)st * C::stage_bytes();
+    T* Ks = reinterpret_cast<T*>(base);
+    T* Vs = reinterpret_cast<T*>(base + NH * C::k_bytes());
+    T* Bs = reinterpret_cast<T*>(base + NH * (C::k_bytes() + C::v_bytes()) + wave * C::b_bytes());
+    const int hh = (lane % LPS) / CPR, chunk = (lane % CPR) * VEC;
 #pragma unroll
     for (int i = 0; i < C::VLD; ++i) {
-      const int key = KPL * i + lane / CPR, chunk = (lane % CPR) * VEC;
-      *reinterpret_cast<uint4*>(Ks + key * C::KP + chunk) = tb.k[i];
-      *reinterpret_cast<uint4*>(Vs + key * VSP + chunk) = tb.v[i];
+      const int key = wave * SPW + i * SPI + lane / LPS;
+      *reinterpret_cast<uint4*>(Ks + (hh * NK + key) * C::KP + chunk) = tb.k[i];
+      *reinterpret_cast<uint4*>(Vs + (hh * NK + key) * VSP + chunk) = tb.v[i];
     }
 #pragma unroll
     for (int m = 0; m < C::BLD; ++m) {
       const int idx = m * 64 + lane;
       *reinterpret_cast<uint4*>(Bs + (idx / C::BCH) * C::BW + (idx % C::BCH) * VEC) = tb.b[m];
     }
-    wave_lds_fence();
+  };
+
+  f32x4 acc[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{};
+  // Softmax reference: the column max of the split's first tile (the four
+  // lanes of a column agree on it).  Later logits may exceed it; P = exp(x -
+  // m_ref) stays finite as long as they exceed it by less than kOver, which
+  // a running check confirms.  If not, the workgroup streams the split a
+  // second time with m_ref = the split's true column max (then no P
+  // exceeds 1).
+  float m_ref = kNegInf, l_run = 0.f;
+  float m_all = kNegInf;        // running max of this lane's logits
+  bool second_pass = false;     // workgroup-uniform
+  uint64_t over = 0;            // lanes that saw x > m_ref + kOver
+
+  // Tile t of this wave's head from LDS stage st.
+  auto compute = [&](int t, int st) {
+    const int kt = s_lo + t * NK;
+    const unsigned char* base = smem + (size_t)st * C::stage_bytes();
+    const T* Ks = reinterpret_cast<const T*>(base) + wave * NK * C::KP;
+    const T* Vs = reinterpret_cast<const T*>(base + NH * C::k_bytes()) + wave * NK * VSP;
+    const T* Bs = reinterpret_cast<const T*>(base + NH * (C::k_bytes() + C::v_bytes()) +
+                                             wave * C::b_bytes());
     // S^T blocks: lane holds head col, keys kt + 16 blk + 4 u4 + i.  A
     // operand: key 16 blk + col, d = 32 st + 8 u4 .. (bf16) or 4 st + u4.
     f32x4 s[2];
@@ -281,11 +329,11 @@ decode_kernel(const DecodeParams P) {
       s[blk] = f32x4{};
       const T* kr = Ks + (16 * blk + col) * C::KP;
 #pragma unroll
-      for (int st = 0; st < C::KSTEPS; ++st) {
+      for (int k = 0; k < C::KSTEPS; ++k) {
         if constexpr (C::kBF16)
-          s[blk] = mfma16(*reinterpret_cast<const bf16x8*>(kr + 32 * st + 8 * u4), qop[st], s[blk]);
+          s[blk] = mfma16(*reinterpret_cast<const bf16x8*>(kr + 32 * k + 8 * u4), qop[k], s[blk]);
         else
-          s[blk] = mfma16(kr[4 * st + u4], qop[st], s[blk]);
+          s[blk] = mfma16(kr[4 * k + u4], qop[k], s[blk]);
       }
     }
     // Bias of key c = 16 blk + i (i < 4) of the lane: distance pq - kt -
@@ -322,93 +370,113 @@ decode_kernel(const DecodeParams P) {
     float x[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = fmaf(s[i >> 2][i & 3], P.scale, bias[i]);
-    if (kt < v_lo || kt + NK > s_hi) {                   // wave-uniform: edge tile
+    if (kt < v_lo || kt + NK > s_hi) {                   // uniform: edge tile
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int j = kt + 16 * (i >> 2) + 4 * u4 + (i & 3);
         x[i] = (j >= v_lo && j < s_hi) ? x[i] : kNegInf;
       }
     }
-    float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                     fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-    // P = exp(x - m_ref) rounded to the input type, row sums from the
-    // rounded values, and O^T += V^T . P^T.
-    auto pv = [&](const float (&xv)[8]) {
-      const float mb = m_ref == kNegInf ? 0.f : m_ref * kLog2e;
-      if constexpr (C::kBF16) {
-        bf16x8 pb;
-        const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
-#pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-          const bf16x2 pr = {from_f32<bf16>(fast_exp2(fmaf(xv[i], kLog2e, -mb))),
-                             from_f32<bf16>(fast_exp2(fmaf(xv[i + 1], kLog2e, -mb)))};
-          pb[i] = pr[0];
-          pb[i + 1] = pr[1];
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
-        }
-        // V^T operand: contraction slots (u4, e) hold keys 4 u4 + e (e < 4)
-        // and 16 + 4 u4 + e - 4 (e >= 4), the keys of pb's slots.  A
-        // transposed read: lane jj of a 16-lane group points at key
-        // 4 u4 + jj / 4, columns 4 (jj % 4) .. +3; lane i receives column i
-        // of those four keys.
-        const int jj = lane & 15;
-        const T* r0 = Vs + (4 * u4 + (jj >> 2)) * VSP + 4 * (jj & 3);
-        const T* r1 = r0 + 16 * VSP;
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(r0 + 16 * dt));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(r1 + 16 * dt));
-          const i16x8 a16 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          acc[dt] = mfma16(__builtin_bit_cast(bf16x8, a16), pb, acc[dt]);
-        }
-      } else {
-        float pf[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          pf[i] = fast_exp2(fmaf(xv[i], kLog2e, -mb));
-          l_run += pf[i];
-        }
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-          const T* vc = Vs + 16 * dt + col;
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            acc[dt] = mfma16(vc[(16 * (i >> 2) + 4 * u4 + (i & 3)) * VSP], pf[i], acc[dt]);
-        }
-      }
-    };
-    if (t == 0 && !second_pass) {                        // wave-uniform
-      float m = fmaxf(mx, xor_lane(mx, 16));
+    const float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                           fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    if (t == 0 && !second_pass) {                        // uniform
+      const float m = fmaxf(mx, xor_lane(mx, 16));
       m_ref = fmaxf(m, xor_lane(m, 32));
     }
     m_all = fmaxf(m_all, mx);
     over |= __builtin_amdgcn_ballot_w64(mx > m_ref + kOver);
-    pv(x);
+    // P = exp(x - m_ref) rounded to the input type, row sums from the
+    // rounded values, and O^T += V^T . P^T.
+    const float mb = m_ref == kNegInf ? 0.f : m_ref * kLog2e;
+    if constexpr (C::kBF16) {
+      bf16x8 pb;
+      const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        const bf16x2 pr = {from_f32<bf16>(fast_exp2(fmaf(x[i], kLog2e, -mb))),
+                           from_f32<bf16>(fast_exp2(fmaf(x[i + 1], kLog2e, -mb)))};
+        pb[i] = pr[0];
+        pb[i + 1] = pr[1];
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
+      }
+      // V^T operand: contraction slots (u4, e) hold keys 4 u4 + e (e < 4)
+      // and 16 + 4 u4 + e - 4 (e >= 4), the keys of pb's slots.  A
+      // transposed read: lane jj of a 16-lane group points at key
+      // 4 u4 + jj / 4, columns 4 (jj % 4) .. +3; lane i receives column i
+      // of those four keys.
+      const int jj = lane & 15;
+      const T* r0 = Vs + (4 * u4 + (jj >> 2)) * VSP + 4 * (jj & 3);
+      const T* r1 = r0 + 16 * VSP;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(r0 + 16 * dt));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(r1 + 16 * dt));
+        const i16x8 a16 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        acc[dt] = mfma16(__builtin_bit_cast(bf16x8, a16), pb, acc[dt]);
+      }
+    } else {
+      float pf[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pf[i] = fast_exp2(fmaf(x[i], kLog2e, -mb));
+        l_run += pf[i];
+      }
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        const T* vc = Vs + 16 * dt + col;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          acc[dt] = mfma16(vc[(16 * (i >> 2) + 4 * u4 + (i & 3)) * VSP], pf[i], acc[dt]);
+      }
+    }
   };
 
-  wave_lds_fence();                                      // page ids visible
-  // Ring of NBUF tile buffers: tile t computes from buffer t % NBUF while
-  // tiles t+1 .. t+DEPTH are in flight.  Loads past the last tile read
-  // nothing (zero-size descriptors), so no load sits under control flow.
-  Tile<T, D> tb[NBUF];
+  // Page ids visible to every wave.
+  if constexpr (NH > 1) wg_lds_barrier(); else wave_lds_fence();
+  // Ring of NBUF tile buffers: tile t is staged from buffer t % NBUF while
+  // tiles t+1 .. t+DEPTH are in flight.  The K rows and bias runs of tile
+  // t+DEPTH are issued before tile t is staged, its V rows after tile t is
+  // computed, so that a wave's K and V requests for the same slots do not
+  // reach memory together.  Loads past the last tile read nothing
+  // (zero-size descriptors), so no load sits under control flow.
+  // With several waves, tile t goes to LDS stage t % 2: the barrier after
+  // staging it also tells every wave that all have finished computing tile
+  // t - 1, whose stage the next tile reuses.
+  Tile<T, D, NH> tb[NBUF];
   while (true) {
 #pragma unroll
-    for (int i = 0; i < DEPTH; ++i) issue(tb[i], i);
+    for (int i = 0; i < DEPTH; ++i) issue(tb[i], i, true, true);
     for (int t0 = 0;; t0 += NBUF) {
 #pragma unroll
       for (int r = 0; r < NBUF; ++r) {
-        issue(tb[(r + DEPTH) % NBUF], t0 + r + DEPTH);
-        compute(tb[r], t0 + r);
-        if (t0 + r + 1 >= ntiles) goto done;
+        const int t = t0 + r;
+        issue(tb[(r + DEPTH) % NBUF], t + DEPTH, true, false);
+        const int st = C::STAGES > 1 ? (t & 1) : 0;
+        if constexpr (NH == 1) wave_lds_fence();
+        stage_tile(tb[r], st);
+        if constexpr (NH > 1) wg_lds_barrier(); else wave_lds_fence();
+        compute(t, st);
+        issue(tb[(r + DEPTH) % NBUF], t + DEPTH, false, true);
+        if (t + 1 >= ntiles) goto done;
       }
     }
   done:
     // Loads past the last tile may still be outstanding; draining them here
     // keeps the compiler's load accounting exact for a second pass.
     __builtin_amdgcn_s_waitcnt(0);
-    if (second_pass || over == 0) break;
+    bool any = over != 0;
+    if constexpr (NH > 1) {
+      if (lane == 0) ovf_lds[wave] = any ? 1 : 0;
+      wg_lds_barrier();
+      any = false;
+#pragma unroll
+      for (int w = 0; w < NH; ++w) any |= ovf_lds[w] != 0;
+      // Every wave has read the flags before any can write them again.
+      wg_lds_barrier();
+    }
+    if (second_pass || !any) break;
     // Rare: some logit exceeded the first tile's max by more than kOver.
     second_pass = true;
     const float m = fmaxf(m_all, xor_lane(m_all, 16));
@@ -479,28 +547,43 @@ combine_kernel(const CombineParams P) {
 
 template <typename T, int D>
 size_t decode_lds_t(const DecodeParams& p) {
-  return Decode<T, D>::fixed_lds() + (size_t)p.pid_cap * 4;
+  size_t fixed = Decode<T, D, 1>::fixed_lds();
+  if constexpr (sizeof(T) == 2) {
+    if (p.heads_per_wg == 4) fixed = Decode<T, D, 4>::fixed_lds();
+    if (p.heads_per_wg == 2) fixed = Decode<T, D, 2>::fixed_lds();
+  }
+  return fixed + (size_t)p.pid_cap * 4;
 }
 
-template <typename T, int D, bool CLAMP>
+template <typename T, int D, bool CLAMP, int NH>
 hipError_t launch_decode_c(const DecodeParams& p, hipStream_t stream) {
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&decode_kernel<T, D, CLAMP>),
+        reinterpret_cast<const void*>(&decode_kernel<T, D, CLAMP, NH>),
         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const dim3 grid(p.hkv, p.num_splits, p.num_seqs);
-  decode_kernel<T, D, CLAMP><<<grid, dim3(64), decode_lds_t<T, D>(p), stream>>>(p);
+  const dim3 grid(p.hkv / NH, p.num_splits, p.num_seqs);
+  decode_kernel<T, D, CLAMP, NH><<<grid, dim3(64 * NH), decode_lds_t<T, D>(p), stream>>>(p);
   return hipGetLastError();
+}
+
+template <typename T, int D, int NH>
+hipError_t launch_decode_h(const DecodeParams& p, hipStream_t stream) {
+  return p.clamp ? launch_decode_c<T, D, true, NH>(p, stream)
+                 : launch_decode_c<T, D, false, NH>(p, stream);
 }
 
 template <typename T, int D>
 hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
-  return p.clamp ? launch_decode_c<T, D, true>(p, stream)
-                 : launch_decode_c<T, D, false>(p, stream);
+  if constexpr (sizeof(T) == 2) {
+    if (p.heads_per_wg == 4) return launch_decode_h<T, D, 4>(p, stream);
+    if (p.heads_per_wg == 2) return launch_decode_h<T, D, 2>(p, stream);
+  }
+  if (p.heads_per_wg != 1) return hipErrorInvalidValue;
+  return launch_decode_h<T, D, 1>(p, stream);
 }
 
 template <typename T, int D>

@@ -136,6 +136,11 @@ DECODE_CASES = [
     ("mha_g1", 35, [700], 4, 4, 128, 0, 1024, [1, 5]),
     ("g16", 36, [450, 33], 32, 2, 128, 0, 512, [1, 6]),
     ("fp32", 37, [300, 77], 8, 4, 64, 100, 100, [1, 4]),
+    # KV heads per decode workgroup: 1 (Hkv odd), 2 (Hkv = 6), and 2 again
+    # when four heads' LDS stages leave no room for a long page-id table.
+    ("hkv3_one_head_per_wg", 38, [500, 40], 6, 3, 128, 0, 1024, [1, 3]),
+    ("hkv6_two_heads_per_wg", 39, [260, 700], 48, 6, 128, 512, 512, [1, 2]),
+    ("long_context_table", 44, [20000, 100], 16, 8, 128, 0, 8192, [1, 0]),
 ]
 
 
@@ -152,27 +157,31 @@ def test_decode_matches_oracle(case):
         U.compare(out, ref, dtype, f"{name}/s{s}")
 
 
-def _bias_spike(b, dist, amount):
-    """Adds `amount` to the bias at one distance (every row and head): the
-    logits of one key per row jump far above the others."""
+def _bias_spike(b, dist, amount, head=None):
+    """Adds `amount` to the bias at one distance (every row; every head, or
+    only query head `head`): the logits of one key per row jump far above
+    the others."""
     rel = b.rel_logits.clone()
-    rel[:, :, dist] = (rel[:, :, dist].float() + amount).to(rel.dtype)
+    hs = slice(None) if head is None else slice(head, head + 1)
+    rel[:, hs, dist] = (rel[:, hs, dist].float() + amount).to(rel.dtype)
     return dataclasses.replace(b, rel_logits=rel)
 
 
-@pytest.mark.parametrize("dist,amount", [(0, 60.0), (0, 30.0), ("far", 60.0)])
-def test_decode_logit_spike(dist, amount):
+@pytest.mark.parametrize("dist,amount,head", [(0, 60.0, None), (0, 30.0, None),
+                                              ("far", 60.0, None), (0, 60.0, 4)])
+def test_decode_logit_spike(dist, amount, head):
     """A logit far above the first tile's (distance 0 sits in the last tile)
     or far below the rest (the farthest key carries the spike): the softmax
-    reference must follow without overflow or loss."""
+    reference must follow without overflow or loss.  With one spiking head
+    the other heads that share its workgroup take the second pass too."""
     b = _mk(42, [2000, 700, 3000], [1, 1, 1], Hq=12, Hkv=4, W=0, R=4096)
     d_ = 600 if dist == "far" else dist
-    b = _bias_spike(b, d_, amount)
+    b = _bias_spike(b, d_, amount, head)
     ref, _ = oracle.run_batch(b)
     d = U.Dev(b)
     for s in (1, 3):
-        _say(f"decode spike dist={dist} amount={amount} splits={s}")
-        U.compare(U.decode(d, splits=s), ref, "bf16", f"spike/{dist}/{amount}/s{s}")
+        _say(f"decode spike dist={dist} amount={amount} head={head} splits={s}")
+        U.compare(U.decode(d, splits=s), ref, "bf16", f"spike/{dist}/{amount}/{head}/s{s}")
 
 
 @pytest.mark.parametrize("dist,amount", [(0, 60.0), (300, 60.0)])
