@@ -147,7 +147,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="local_decode",
                     choices=["local_decode", "global_decode", "local_prefill",
-                             "global_mixed", "global_mixed_split", "tiny_prefill"])
+                             "global_mixed", "global_mixed_split", "tiny_prefill",
+                             "long_global_decode"])
     ap.add_argument("--splits", type=int, default=0, help="decode num_splits (0 = library)")
     ap.add_argument("--replicas", type=int, default=0, help="input copies rotated (0 = auto)")
     ap.add_argument("--seed", type=int, default=0)
@@ -290,7 +291,8 @@ def main():
 
     achieved = step_bytes / (launch_ms * 1e-3) / 1e9
     tflops = step_flops / (launch_ms * 1e-3) / 1e12
-    kernel_src = DECODE_KERNEL_SRC if wl in ("local_decode", "global_decode") else PREFILL_KERNEL_SRC
+    kernel_src = (DECODE_KERNEL_SRC if wl in ("local_decode", "global_decode", "long_global_decode")
+                  else PREFILL_KERNEL_SRC)
     traffic = traffic_from_profiles(wl, kernel_src)
     peak_tf = BF16_PEAK_TFLOPS if batch.dtype == "bf16" else FP32_PEAK_TFLOPS
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,

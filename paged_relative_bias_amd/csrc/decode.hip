@@ -39,8 +39,8 @@
 // bias; masking by select only on the first and last tile of the split;
 // softmax against a fixed reference (the column max of the split's first
 // tile) with a second pass over the split, taken by the whole workgroup, in
-// the rare case that a later logit exceeds it by more than kOver; P rounded
-// to bf16 with its row sum taken from the rounded values; O^T[d][head] +=
+// the rare case that a later logit exceeds it by more than kOver; P as the
+// sum of two bf16 terms (hi + lo) with an fp32 row sum; O^T[d][head] +=
 // V^T . P^T.  One split writes the output; otherwise each wave writes its
 // normalised partial and log-sum-exp, and combine_kernel merges them in
 // split order (no atomics).
@@ -54,7 +54,6 @@ namespace {
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Largest logit excess over the reference (natural units) for which P =
 // exp(x - m_ref) and the running sums stay far from fp32 / bf16 overflow.
@@ -385,22 +384,23 @@ decode_kernel(const DecodeParams P) {
     }
     m_all = fmaxf(m_all, mx);
     over |= __builtin_amdgcn_ballot_w64(mx > m_ref + kOver);
-    // P = exp(x - m_ref) rounded to the input type, row sums from the
-    // rounded values, and O^T += V^T . P^T.
+    // P = exp(x - m_ref), and O^T += V^T . P^T.
     const float mb = m_ref == kNegInf ? 0.f : m_ref * kLog2e;
     if constexpr (C::kBF16) {
-      bf16x8 pb;
-      const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+      // P enters the PV product as two bf16 terms, hi = RNE(P) and lo =
+      // RNE(P - hi), whose sum is P to 2^-17 relative; a single bf16 P would
+      // move an output by up to 2^-9 of the spread of V.
+      bf16x8 ph, pl;
 #pragma unroll
-      for (int i = 0; i < 8; i += 2) {
-        const bf16x2 pr = {from_f32<bf16>(fast_exp2(fmaf(x[i], kLog2e, -mb))),
-                           from_f32<bf16>(fast_exp2(fmaf(x[i + 1], kLog2e, -mb)))};
-        pb[i] = pr[0];
-        pb[i + 1] = pr[1];
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
+      for (int i = 0; i < 8; ++i) {
+        const float pf = fast_exp2(fmaf(x[i], kLog2e, -mb));
+        const bf16 h = from_f32<bf16>(pf);
+        ph[i] = h;
+        pl[i] = from_f32<bf16>(pf - (float)h);
+        l_run += pf;
       }
       // V^T operand: contraction slots (u4, e) hold keys 4 u4 + e (e < 4)
-      // and 16 + 4 u4 + e - 4 (e >= 4), the keys of pb's slots.  A
+      // and 16 + 4 u4 + e - 4 (e >= 4), the keys of ph's and pl's slots.  A
       // transposed read: lane jj of a 16-lane group points at key
       // 4 u4 + jj / 4, columns 4 (jj % 4) .. +3; lane i receives column i
       // of those four keys.
@@ -414,7 +414,8 @@ decode_kernel(const DecodeParams P) {
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) i16x4*)(r1 + 16 * dt));
         const i16x8 a16 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        acc[dt] = mfma16(__builtin_bit_cast(bf16x8, a16), pb, acc[dt]);
+        acc[dt] = mfma16(__builtin_bit_cast(bf16x8, a16), ph, acc[dt]);
+        acc[dt] = mfma16(__builtin_bit_cast(bf16x8, a16), pl, acc[dt]);
       }
     } else {
       float pf[8];

@@ -38,8 +38,9 @@
 //                                 more than kOver above it streams its keys
 //                                 a second time with the exact column max
 //   O^T[d][col] += V^T . P^T      V^T operand from ds_read_tr16_b64, P^T
-//                                 from registers; row sums of the rounded P
-//                                 with v_dot2_f32_bf16.
+//                                 from registers as two bf16 terms (hi =
+//                                 RNE(P), lo = RNE(P - hi)), two MFMAs;
+//                                 row sums of P in fp32.
 #include <type_traits>
 
 #include "device.hpp"
@@ -50,7 +51,6 @@ namespace {
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Largest logit excess over the reference (natural units) for which P =
 // exp(x - m_ref) and the running sums stay far from fp32 / bf16 overflow.
@@ -359,20 +359,20 @@ prefill_kernel(const PrefillParams P) {
     over |= __builtin_amdgcn_ballot_w64(cval && mx > m_ref + kOver);
     const float mb = m_ref == kNegInf ? 0.f : m_ref * kLog2e;
     if constexpr (C::kBF16) {
-      bf16x8 pb[2];
-      const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+      // P enters the PV product as two bf16 terms, hi = RNE(P) and lo =
+      // RNE(P - hi), whose sum is P to 2^-17 relative; a single bf16 P would
+      // move an output by up to 2^-9 of the spread of V.
+      bf16x8 ph[2], pl[2];
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const bf16x2 pr = {from_f32<bf16>(fast_exp2(fmaf(x[i], kLog2e, -mb))),
-                           from_f32<bf16>(fast_exp2(fmaf(x[i + 1], kLog2e, -mb)))};
-        pb[i >> 3][i & 7] = pr[0];
-        pb[i >> 3][(i & 7) + 1] = pr[1];
-        // The row sum uses the rounded values, so the weights applied to V
-        // are exactly normalised.
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
+      for (int i = 0; i < 16; ++i) {
+        const float pf = fast_exp2(fmaf(x[i], kLog2e, -mb));
+        const bf16 h = from_f32<bf16>(pf);
+        ph[i >> 3][i & 7] = h;
+        pl[i >> 3][i & 7] = from_f32<bf16>(pf - (float)h);
+        l_run += pf;
       }
       // V^T operand for 16 keys ks*16 + slots (u, e): keys 16ks + 4u + e
-      // (e < 4) and 16ks + 8 + 4u + e - 4 (e >= 4), matching pb[ks].  The
+      // (e < 4) and 16ks + 8 + 4u + e - 4 (e >= 4), matching ph/pl[ks].  The
       // 16-lane groups of a transposed read cover d0..d0+15: lane j points
       // at key (4u + j/4), columns d0 + 4*(j%4) .. +3.
       const int jj = lane & 15;
@@ -387,7 +387,8 @@ prefill_kernel(const PrefillParams P) {
           const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (__attribute__((address_space(3))) i16x4*)(vb + (16 * ks + 8) * VP));
           const i16x8 a16 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          acc[dt] = mfma32(__builtin_bit_cast(bf16x8, a16), pb[ks], acc[dt]);
+          acc[dt] = mfma32(__builtin_bit_cast(bf16x8, a16), ph[ks], acc[dt]);
+          acc[dt] = mfma32(__builtin_bit_cast(bf16x8, a16), pl[ks], acc[dt]);
         }
       }
     } else {

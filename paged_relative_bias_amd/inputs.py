@@ -265,12 +265,25 @@ def global_mixed(seed: int = 0, n_decode: int = 48, n_chunks: int = 4,
                       name="global_mixed")
 
 
+def long_global_decode(seed: int = 0, batch: int = 4, lo: int = 32768,
+                       hi: int = 240000, poison: bool = True) -> Batch:
+    """4 sequences, contexts U[32768, 240000], Hq=48, Hkv=8, full causal,
+    R=8192 (distances past 8191 read the last entry)."""
+    rng = np.random.default_rng(seed)
+    L = rng.integers(lo, hi + 1, size=batch)
+    return make_batch(rng, L, np.ones_like(L), num_q_heads=HQ,
+                      num_kv_heads=HKV_GLOBAL, head_dim=HEAD_DIM, window=0,
+                      rel_len=MAX_CONTEXT, max_blocks_per_seq=(hi + BLOCK_SIZE - 1) // BLOCK_SIZE,
+                      poison=poison, name="long_global_decode")
+
+
 WORKLOADS = {
     "tiny_prefill": tiny,
     "local_decode": local_decode,
     "global_decode": global_decode,
     "local_prefill": local_prefill,
     "global_mixed": global_mixed,
+    "long_global_decode": long_global_decode,
 }
 
 

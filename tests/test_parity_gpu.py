@@ -67,6 +67,12 @@ PREFILL_CASES = [
     ("g16_bq16", 11, [170], [170], 32, 2, 128, 48, 48, "bf16"),
     ("fp32_d128", 12, [150, 20], [150, 20], 8, 4, 128, 40, 40, "fp32"),
     ("zero_len_seq", 13, [300, 5, 90], [300, 0, 90], 12, 4, 128, 64, 64, "bf16"),
+    # Per-GPU head counts under tensor parallelism (48 query heads; 16 local
+    # / 8 global KV heads) at TP = 8 and TP = 4.
+    ("tp8_local", 14, [900, 130], [900, 130], 6, 2, 128, 512, 512, "bf16"),
+    ("tp8_global", 15, [1200, 300], [600, 300], 6, 1, 128, 0, 8192, "bf16"),
+    ("tp4_local", 16, [700, 40], [700, 40], 12, 4, 128, 512, 512, "bf16"),
+    ("tp4_global", 17, [800, 64], [400, 64], 12, 2, 128, 0, 8192, "bf16"),
 ]
 
 
@@ -141,6 +147,11 @@ DECODE_CASES = [
     ("hkv3_one_head_per_wg", 38, [500, 40], 6, 3, 128, 0, 1024, [1, 3]),
     ("hkv6_two_heads_per_wg", 39, [260, 700], 48, 6, 128, 512, 512, [1, 2]),
     ("long_context_table", 44, [20000, 100], 16, 8, 128, 0, 8192, [1, 0]),
+    # Per-GPU head counts under tensor parallelism at TP = 8 and TP = 4.
+    ("tp8_local", 45, [600, 2000, 33], 6, 2, 128, 512, 512, [1, 2, 0]),
+    ("tp8_global", 46, [5000, 700, 8192], 6, 1, 128, 0, 8192, [1, 8, 0]),
+    ("tp4_local", 48, [1500, 513], 12, 4, 128, 512, 512, [1, 0]),
+    ("tp4_global", 47, [3000, 4100], 12, 2, 128, 0, 8192, [1, 4, 0]),
 ]
 
 
@@ -238,6 +249,18 @@ def test_full_global_decode(splits):
     _say(f"full global_decode splits={splits}")
     ref, _ = oracle.run_batch(b)
     U.compare(U.decode(U.Dev(b), splits=splits), ref, "bf16", f"global_decode/s{splits}")
+
+
+@pytest.mark.timeout(400)
+def test_full_long_global_decode():
+    """Contexts of 32K-240K keys (R = 8192, so the clamp is active) with the
+    library's split count and the 128-split cap."""
+    b = _full("long_global_decode")
+    ref, _ = oracle.run_batch(b)
+    d = U.Dev(b)
+    for s in (0, 32, 128):
+        _say(f"full long_global_decode L={b.seq_lens.tolist()} splits={s}")
+        U.compare(U.decode(d, splits=s), ref, "bf16", f"long_global_decode/s{s}")
 
 
 @pytest.mark.timeout(400)
