@@ -322,7 +322,10 @@ prefill_kernel(const PrefillParams P) {
     const bool unclamped = (wje - 1) - kt <= R - 1;       // wave-uniform
     const bool full = (W <= 0 || (wje - 1) - kt < W) && (pbase + wt_lo) - (kt + N - 1) >= 0;
     if (unclamped) {
-      const T* bb = brow + (D0 - base_c - 27);
+      // Entries start .. start + 27 of the staged run; for real columns
+      // start + 27 <= SB - 1 on these tiles, and the bound keeps padding
+      // columns' reads inside the staging area as well.
+      const T* bb = brow + imin(D0 - base_c - 27, SB - 28);
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         x[i] = fmaf(s[i], P.scale, to_f32(bb[27 - (8 * (i >> 2) + (i & 3))]));
@@ -409,26 +412,26 @@ prefill_kernel(const PrefillParams P) {
   };
 
   // ---- software pipeline over key tiles ----------------------------------
-  // Two register buffers keep two tiles in flight: at the top of each step
-  // tile kt sits in an LDS stage, tile kt+N in one buffer (issued a step
-  // earlier) and tile kt+2N is issued into the other.  Loads past the last
-  // tile read nothing, so no load sits under control flow.
-  Regs ra, rb;
+  // One register buffer: at the top of each step tile kt sits in an LDS
+  // stage and tile kt+N is issued into the buffer; it lands while tile kt
+  // is computed and goes to the other stage after.  (A second buffer, for
+  // a tile more in flight, measured no faster and costs 28 VGPRs.)  Loads
+  // past the last tile read nothing, so no load sits under control flow.
+  Regs ra;
   while (true) {
     lds_barrier();                                       // page ids ready
     int kt = jb & ~15;
     issue(ra, kt);
-    issue(rb, kt + N);
     commit(ra, 0);
     lds_barrier();
     while (true) {
-      issue(ra, kt + 2 * N);
+      issue(ra, kt + N);
       compute(kt, 0);
       if (kt + N >= je) break;                           // workgroup-uniform
-      commit(rb, 1);
+      commit(ra, 1);
       lds_barrier();
       kt += N;
-      issue(rb, kt + 2 * N);
+      issue(ra, kt + N);
       compute(kt, 1);
       if (kt + N >= je) break;
       commit(ra, 0);
