@@ -152,6 +152,10 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="decode num_splits (0 = library)")
     ap.add_argument("--replicas", type=int, default=0, help="input copies rotated (0 = auto)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--batch", type=int, default=0,
+                    help="sequences in a decode workload (0 = the workload's own)")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture each replica's step once in a HIP graph and time replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (counter calibration) and exit")
@@ -204,7 +208,10 @@ def main():
     split_mixed = wl == "global_mixed_split"
     gen = inputs.WORKLOADS["global_mixed" if split_mixed else wl]
     t0 = time.perf_counter()
-    batch = gen(seed=args.seed)
+    if args.batch and not wl.endswith("decode"):
+        log("--batch applies to the decode workloads only")
+        sys.exit(2)
+    batch = gen(seed=args.seed, batch=args.batch) if args.batch else gen(seed=args.seed)
     log(f"generated {batch.name} in {time.perf_counter() - t0:.1f}s: B={batch.num_seqs} "
         f"total_q={batch.total_q} Hq={batch.num_q_heads} Hkv={batch.num_kv_heads} "
         f"D={batch.head_dim} W={batch.window} R={batch.rel_len}")
@@ -215,7 +222,10 @@ def main():
     step_flops = sum(a["flops"] for a in alg)
     replicas = args.replicas or max(2, math.ceil(2 * MALL_BYTES / step_bytes) + 1)
 
+    # With --graph the calls are issued on a side stream that is captured;
+    # the replays then run on the current stream.
     stream = torch.cuda.current_stream()
+    launch_stream = torch.cuda.Stream() if args.graph else stream
     calls = []       # per replica: list of (fn_name, args)
     keep = []        # tensors and dims that must stay alive
     splits_used = []
@@ -236,7 +246,7 @@ def main():
                 ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev) if need else None
                 a, dims = binding.decode_args(q, k, v, bt, sl, rel, p.window, p.scale, out,
                                               max_seq_len=p.max_seq_len, num_splits=s,
-                                              workspace=ws, stream=stream)
+                                              workspace=ws, stream=launch_stream)
                 rc.append(("inkling_rel_attn_decode", a))
                 keep += [q, k, v, rel, bt, sl, out, ws, dims]
                 if r == 0:
@@ -245,7 +255,7 @@ def main():
                 cu = torch.from_numpy(p.cu_q_lens).to(dev)
                 a, dims = binding.prefill_args(q, k, v, bt, sl, cu, rel, p.window, p.scale,
                                                out, max_q_len=p.max_q_len,
-                                               max_seq_len=p.max_seq_len, stream=stream)
+                                               max_seq_len=p.max_seq_len, stream=launch_stream)
                 rc.append(("inkling_rel_attn_prefill", a))
                 keep += [q, k, v, rel, bt, sl, cu, out, dims]
         calls.append(rc)
@@ -253,11 +263,30 @@ def main():
     lib = binding.load()
     fns = [[(getattr(lib, name), a) for name, a in rc] for rc in calls]
 
-    def step(i):
+    def eager_step(i):
         for fn, a in fns[i % replicas]:
             st = fn(*a)
             if st != 0:
                 raise binding.InklingError(st, "step")
+
+    step = eager_step
+    if args.graph:
+        # One eager run per replica on the capture stream (kernel attributes
+        # are set on first use), then one capture per replica.
+        with torch.cuda.stream(launch_stream):
+            for r in range(replicas):
+                eager_step(r)
+        launch_stream.synchronize()
+        graphs = []
+        for r in range(replicas):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=launch_stream):
+                eager_step(r)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+        def step(i):
+            graphs[i % replicas].replay()
 
     for i in range(args.warmup):
         step(i)
@@ -321,7 +350,7 @@ def main():
            "head_dim": batch.head_dim, "window": batch.window, "rel_len": batch.rel_len,
            "block_size": batch.block_size, "seq_lens_sum": int(batch.seq_lens.sum()),
            "max_seq_len": int(batch.max_seq_len), "num_splits": splits_used or None,
-           "replicas": replicas, "seed": args.seed}
+           "replicas": replicas, "seed": args.seed, "launch": "hip_graph" if args.graph else "eager"}
     rec = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,

@@ -120,6 +120,10 @@ def test_split_heuristic_bounds():
     one = _dims(num_seqs=1, total_q=1, num_kv_heads=1, num_q_heads=1)
     assert B.num_splits(one, 0, -1) == 32       # 8192 keys / 256 per split
     assert B.load().inkling_rel_attn_num_splits(None, 0, -1) == 1
+    # A lone 512-key window (17 tiles) on an empty GPU: down to ~2 tiles
+    # per split.
+    assert B.num_splits(_dims(num_seqs=1, total_q=1), 512, -1) == 8
+    assert B.num_splits(_dims(num_seqs=16, total_q=16), 512, -1) == 4
 
 
 def test_status_strings_and_device_check_without_gpu():
