@@ -154,6 +154,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--batch", type=int, default=0,
                     help="sequences in a decode workload (0 = the workload's own)")
+    ap.add_argument("--append", action="store_true",
+                    help="decode workloads: inkling_rel_attn_decode_append (the step's K/V "
+                         "rows stored into the cache in the same launch)")
     ap.add_argument("--graph", action="store_true",
                     help="capture each replica's step once in a HIP graph and time replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -217,8 +220,15 @@ def main():
         f"D={batch.head_dim} W={batch.window} R={batch.rel_len}")
     parts = list(inputs.split_mixed(batch)) if split_mixed else [batch]
     parts = [p for p in parts if p.num_seqs > 0]
+    if args.append and not wl.endswith("decode"):
+        log("--append applies to the decode workloads only")
+        sys.exit(2)
     alg = [algorithmic(p) for p in parts]
     step_bytes = sum(a["bytes"] for a in alg)
+    if args.append:
+        # k_new and v_new read once, and the same rows written to the cache.
+        step_bytes += 2 * 2 * batch.num_seqs * batch.num_kv_heads * batch.head_dim * (
+            2 if batch.dtype == "bf16" else 4)
     step_flops = sum(a["flops"] for a in alg)
     replicas = args.replicas or max(2, math.ceil(2 * MALL_BYTES / step_bytes) + 1)
 
@@ -247,7 +257,16 @@ def main():
                 a, dims = binding.decode_args(q, k, v, bt, sl, rel, p.window, p.scale, out,
                                               max_seq_len=p.max_seq_len, num_splits=s,
                                               workspace=ws, stream=launch_stream)
-                rc.append(("inkling_rel_attn_decode", a))
+                if args.append:
+                    # The new token's rows are the ones already at key L - 1.
+                    kn = torch.stack([p.k_logical[i][int(p.seq_lens[i]) - 1]
+                                      for i in range(p.num_seqs)]).to(dev)
+                    vn = torch.stack([p.v_logical[i][int(p.seq_lens[i]) - 1]
+                                      for i in range(p.num_seqs)]).to(dev)
+                    a = a[:1] + (binding._ptr(kn), binding._ptr(vn)) + a[1:]
+                    keep += [kn, vn]
+                rc.append(("inkling_rel_attn_decode_append" if args.append
+                           else "inkling_rel_attn_decode", a))
                 keep += [q, k, v, rel, bt, sl, out, ws, dims]
                 if r == 0:
                     splits_used.append(s)
@@ -350,7 +369,8 @@ def main():
            "head_dim": batch.head_dim, "window": batch.window, "rel_len": batch.rel_len,
            "block_size": batch.block_size, "seq_lens_sum": int(batch.seq_lens.sum()),
            "max_seq_len": int(batch.max_seq_len), "num_splits": splits_used or None,
-           "replicas": replicas, "seed": args.seed, "launch": "hip_graph" if args.graph else "eager"}
+           "replicas": replicas, "seed": args.seed, "launch": "hip_graph" if args.graph else "eager",
+           "append": bool(args.append)}
     rec = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,

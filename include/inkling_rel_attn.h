@@ -125,6 +125,31 @@ inkling_status_t inkling_rel_attn_decode(
     const inkling_rel_attn_dims_t* dims, void* stream);
 
 /*
+ * Decode that also appends this step's K/V rows to the cache, in the same
+ * launch.  The TensorRT-LLM Inkling page's pull request (commit list, the
+ * clean-up of the attention op's arguments) shows an attention op that
+ * writes the new K/V itself unless told to skip it.  Same inputs, outputs
+ * and errors as inkling_rel_attn_decode, plus:
+ *   k_new, v_new  [num_seqs, Hkv, head_dim] in the cache dtype: the K and V
+ *                 rows of each sequence's new token (position L_b - 1).
+ *                 Row b is stored into page block_table[b][(L_b - 1) / 16],
+ *                 slot (L_b - 1) % 16, and the attention uses it as key
+ *                 L_b - 1 whatever that slot held before.  Sequences with
+ *                 L_b = 0 store nothing.
+ *   k_cache, v_cache  read and written.  No two sequences may map key
+ *                 L_b - 1 to the same slot; k_new / v_new must not overlap
+ *                 the caches.
+ * Null k_new or v_new (with num_seqs > 0) is INKLING_ERR_INVALID_ARGUMENT.
+ * Later work on the stream sees the stored rows.
+ */
+inkling_status_t inkling_rel_attn_decode_append(
+    const void* q, const void* k_new, const void* v_new, void* k_cache,
+    void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+    const void* rel_logits, int32_t window, float scale, int32_t num_splits,
+    void* workspace, size_t workspace_bytes, void* out,
+    const inkling_rel_attn_dims_t* dims, void* stream);
+
+/*
  * Split count the library would use for a decode call with these shapes
  * (1..128).  Chosen from the device's compute-unit count, B * Hkv and the
  * keys per sequence (window on local layers, max_seq_len on global ones).

@@ -24,6 +24,7 @@ DTYPE_BF16, DTYPE_FP32 = 0, 1
 SYMBOLS = (
     "inkling_rel_attn_prefill",
     "inkling_rel_attn_decode",
+    "inkling_rel_attn_decode_append",
     "inkling_rel_attn_num_splits",
     "inkling_rel_attn_decode_workspace_bytes",
     "inkling_rel_attn_check_device",
@@ -63,6 +64,9 @@ def load(path: str = LIB_PATH):
     lib.inkling_rel_attn_decode.restype = ctypes.c_int
     lib.inkling_rel_attn_decode.argtypes = [P, P, P, P, P, P, I32, F32, I32, P,
                                             ctypes.c_size_t, P, DP, P]
+    lib.inkling_rel_attn_decode_append.restype = ctypes.c_int
+    lib.inkling_rel_attn_decode_append.argtypes = [P, P, P, P, P, P, P, P, I32, F32, I32, P,
+                                                   ctypes.c_size_t, P, DP, P]
     lib.inkling_rel_attn_num_splits.restype = I32
     lib.inkling_rel_attn_num_splits.argtypes = [DP, I32, I32]
     lib.inkling_rel_attn_decode_workspace_bytes.restype = ctypes.c_size_t
@@ -175,6 +179,27 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, rel_logits,
         ctypes.byref(dims), _stream(stream))
     if st != OK:
         raise InklingError(st, "inkling_rel_attn_decode")
+
+
+def decode_append(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens,
+                  rel_logits, window: int, scale: float, out, *, max_seq_len: int,
+                  num_splits: int = 0, workspace=None, stream=None) -> None:
+    """inkling_rel_attn_decode_append on device tensors: decode that also
+    stores k_new / v_new ([B, Hkv, D]) at key L_b - 1 of each sequence."""
+    dims = dims_for(q, k_cache, block_table, rel_logits,
+                    num_seqs=seq_lens.shape[0], max_q_len=1,
+                    max_seq_len=max_seq_len)
+    need = decode_workspace_bytes(dims, window, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().inkling_rel_attn_decode_append(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+        _ptr(block_table), _ptr(seq_lens), _ptr(rel_logits), int(window),
+        float(scale), int(num_splits), _ptr(workspace), ws_bytes, _ptr(out),
+        ctypes.byref(dims), _stream(stream))
+    if st != OK:
+        raise InklingError(st, "inkling_rel_attn_decode_append")
 
 
 # --- pre-marshalled calls (for timing loops: no per-call Python work) -----

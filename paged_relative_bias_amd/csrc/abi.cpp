@@ -218,12 +218,16 @@ inkling_status_t inkling_rel_attn_prefill(const void* q, const void* k_cache, co
   return e == hipSuccess ? INKLING_OK : INKLING_ERR_LAUNCH;
 }
 
-inkling_status_t inkling_rel_attn_decode(const void* q, const void* k_cache, const void* v_cache,
-                                         const int32_t* block_table, const int32_t* seq_lens,
-                                         const void* rel_logits, int32_t window, float scale,
-                                         int32_t num_splits, void* workspace,
-                                         size_t workspace_bytes, void* out,
-                                         const inkling_rel_attn_dims_t* dims, void* stream) {
+}  // extern "C"
+
+namespace {
+
+inkling_status_t decode_impl(const void* q, const void* k_new, const void* v_new,
+                             const void* k_cache, const void* v_cache,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             const void* rel_logits, int32_t window, float scale,
+                             int32_t num_splits, void* workspace, size_t workspace_bytes,
+                             void* out, const inkling_rel_attn_dims_t* dims, void* stream) {
   inkling_status_t st = check_dims(dims);
   if (st != INKLING_OK) return st;
   if (!std::isfinite(scale)) return INKLING_ERR_INVALID_ARGUMENT;
@@ -250,6 +254,8 @@ inkling_status_t inkling_rel_attn_decode(const void* q, const void* k_cache, con
   p.q = q;
   p.k = k_cache;
   p.v = v_cache;
+  p.k_new = k_new;
+  p.v_new = v_new;
   p.block_table = block_table;
   p.seq_lens = seq_lens;
   p.rel = rel_logits;
@@ -310,6 +316,31 @@ inkling_status_t inkling_rel_attn_decode(const void* q, const void* k_cache, con
     if (e != hipSuccess) return INKLING_ERR_LAUNCH;
   }
   return INKLING_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+inkling_status_t inkling_rel_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                                         const int32_t* block_table, const int32_t* seq_lens,
+                                         const void* rel_logits, int32_t window, float scale,
+                                         int32_t num_splits, void* workspace,
+                                         size_t workspace_bytes, void* out,
+                                         const inkling_rel_attn_dims_t* dims, void* stream) {
+  return decode_impl(q, nullptr, nullptr, k_cache, v_cache, block_table, seq_lens, rel_logits,
+                     window, scale, num_splits, workspace, workspace_bytes, out, dims, stream);
+}
+
+inkling_status_t inkling_rel_attn_decode_append(
+    const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+    const int32_t* block_table, const int32_t* seq_lens, const void* rel_logits, int32_t window,
+    float scale, int32_t num_splits, void* workspace, size_t workspace_bytes, void* out,
+    const inkling_rel_attn_dims_t* dims, void* stream) {
+  if (dims != nullptr && dims->num_seqs > 0 && (k_new == nullptr || v_new == nullptr))
+    return INKLING_ERR_INVALID_ARGUMENT;
+  return decode_impl(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens, rel_logits,
+                     window, scale, num_splits, workspace, workspace_bytes, out, dims, stream);
 }
 
 }  // extern "C"

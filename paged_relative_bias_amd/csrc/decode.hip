@@ -71,6 +71,7 @@ struct Decode {
   static constexpr int SPW = NK / NH;                    // slots each wave loads per tile
   static constexpr int VLD = SPW / SPI;                  // K (and V) loads per wave and tile
   static_assert(LPS <= 64 && SPW % SPI == 0 && 16 % SPI == 0, "load layout");
+  static_assert(2 * CPR <= 64, "one K and one V row per wave load");
   static constexpr int KP = D + VEC;                     // K row pitch (elements)
   static constexpr int VSP = kBF16 ? D + 16 : D + 4;     // V row pitch (elements)
   static constexpr int KSTEPS = kBF16 ? D / 32 : D / 4;  // MFMA k-steps per 16 keys
@@ -174,6 +175,20 @@ decode_kernel(const DecodeParams P) {
   const int s_lo = kb0 + split * CT * NK;
   const int s_hi = imin(L, s_lo + CT * NK);
   const int v_lo = imax(s_lo, k_lo);                     // visible keys [v_lo, s_hi)
+
+  // Append: the workgroup whose split ends at key L - 1 stores this step's
+  // K/V rows of its heads into that key's cache slot, and uses them for the
+  // key (its own loads of the slot may see the old contents).  Lanes
+  // [0, CPR) hold the K row's 16-byte chunks, lanes [CPR, 2 CPR) the V row's.
+  // The rows are loaded here and stored once the page ids are in LDS.
+  const bool app = P.k_new != nullptr && s_hi == L;      // uniform
+  uint4 new_chunk = make_uint4(0u, 0u, 0u, 0u);
+  if (app && lane < 2 * CPR) {
+    const bool isv = lane >= CPR;
+    const int64_t row = (int64_t)b * P.hkv + g;
+    new_chunk = *reinterpret_cast<const uint4*>(static_cast<const char*>(isv ? P.v_new : P.k_new) +
+                                                row * D * SZ + (isv ? lane - CPR : lane) * 16);
+  }
 
   // Page ids of the split (and zeros past its end, read by the prefetches
   // beyond the last tile) into LDS.
@@ -436,6 +451,13 @@ decode_kernel(const DecodeParams P) {
 
   // Page ids visible to every wave.
   if constexpr (NH > 1) wg_lds_barrier(); else wave_lds_fence();
+  if (app && lane < 2 * CPR) {
+    const bool isv = lane >= CPR;
+    const int64_t slot = (int64_t)pid_lds[((L - 1) >> 4) - pg_base] * 16 + ((L - 1) & 15);
+    char* dst = static_cast<char*>(const_cast<void*>(isv ? P.v : P.k)) +
+                (slot * P.hkv + g) * D * SZ + (isv ? lane - CPR : lane) * 16;
+    *reinterpret_cast<uint4*>(dst) = new_chunk;
+  }
   // Ring of NBUF tile buffers: tile t is staged from buffer t % NBUF while
   // tiles t+1 .. t+DEPTH are in flight.  The K rows and bias runs of tile
   // t+DEPTH are issued before tile t is staged, its V rows after tile t is
@@ -458,6 +480,20 @@ decode_kernel(const DecodeParams P) {
         if constexpr (NH == 1) wave_lds_fence();
         stage_tile(tb[r], st);
         if constexpr (NH > 1) wg_lds_barrier(); else wave_lds_fence();
+        if (app && t == ntiles - 1) {                    // uniform: holds key L - 1
+          // Only this wave reads its head's rows, so no barrier is needed.
+          const int key = L - 1 - (s_lo + t * NK);
+          unsigned char* base = smem + (size_t)st * C::stage_bytes();
+          if (lane < CPR) {
+            T* Ks = reinterpret_cast<T*>(base) + (wave * NK + key) * C::KP + lane * VEC;
+            *reinterpret_cast<uint4*>(Ks) = new_chunk;
+          } else if (lane < 2 * CPR) {
+            T* Vs = reinterpret_cast<T*>(base + NH * C::k_bytes()) + (wave * NK + key) * VSP +
+                    (lane - CPR) * VEC;
+            *reinterpret_cast<uint4*>(Vs) = new_chunk;
+          }
+          wave_lds_fence();
+        }
         compute(t, st);
         issue(tb[(r + DEPTH) % NBUF], t + DEPTH, false, true);
         if (t + 1 >= ntiles) goto done;

@@ -49,6 +49,8 @@ struct DecodeParams {
   const int32_t* seq_lens;
   const void* rel;
   void* out;          // final output (num_splits == 1)
+  const void* k_new;  // [B, Hkv, D] rows stored at key L_b - 1 and used as it
+  const void* v_new;  //   (both null: no append)
   float* part_o;      // [splits, B, Hq, D] normalised partial outputs
   float* part_lse;    // [splits, B, Hq]
   int32_t num_seqs, hq, hkv, group;

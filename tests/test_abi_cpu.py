@@ -110,6 +110,15 @@ def test_workspace_size_formula():
     assert B.decode_workspace_bytes(d, 0, 129) == 0
 
 
+def test_decode_append_needs_new_rows():
+    # Rejected before any device work: null k_new / v_new.
+    d = _dims(num_seqs=4, total_q=4)
+    st = B.load().inkling_rel_attn_decode_append(
+        None, None, None, None, None, None, None, None, 512, 1.0, 1, None, 0, None,
+        ctypes.byref(d), None)
+    assert st == 1   # INKLING_ERR_INVALID_ARGUMENT
+
+
 def test_split_heuristic_bounds():
     # 64 x 16 units already give four per compute unit on 256 CUs.
     assert B.num_splits(_dims(num_seqs=64, total_q=64), 512, -1) == 1

@@ -218,6 +218,39 @@ def test_decode_equals_last_prefill_row():
     assert diff <= 2e-2, diff   # two bf16 paths, each within 1e-2 of exact
 
 
+@pytest.mark.parametrize("W,R,Hq,Hkv,D,dtype,splits", [
+    (512, 512, 48, 16, 128, "bf16", 1), (512, 512, 48, 16, 128, "bf16", 4),
+    (0, 8192, 48, 8, 128, "bf16", 0), (0, 1024, 6, 3, 128, "bf16", 2),
+    (100, 100, 8, 4, 64, "fp32", 3)])
+def test_decode_append(W, R, Hq, Hkv, D, dtype, splits):
+    """Decode with the new token's K/V stored in the same launch: the slot
+    of key L-1 holds NaN beforehand, the output must match the oracle on the
+    intended cache, and afterwards the whole cache must equal it bit for
+    bit (the new rows in place, nothing else touched)."""
+    L = [1, 16, 17, 33, 700, 2049]
+    b = _mk(50 + Hkv, L, [1] * len(L), Hq=Hq, Hkv=Hkv, D=D, W=W, R=R, dtype=dtype)
+    k_new = torch.stack([b.k_logical[i][L[i] - 1] for i in range(len(L))]).contiguous()
+    v_new = torch.stack([b.v_logical[i][L[i] - 1] for i in range(len(L))]).contiguous()
+    d = U.Dev(b)
+    for i, l in enumerate(L):
+        page = int(b.block_table[i, (l - 1) // 16])
+        d.k[page, (l - 1) % 16] = float("nan")
+        d.v[page, (l - 1) % 16] = float("nan")
+    out = torch.full_like(d.q, float("nan"))
+    _say(f"decode append W={W} Hkv={Hkv} D={D} {dtype} splits={splits}")
+    binding.decode_append(d.q, k_new.cuda(), v_new.cuda(), d.k, d.v, d.bt, d.sl, d.rel, W,
+                          b.scale, out, max_seq_len=b.max_seq_len, num_splits=splits)
+    torch.cuda.synchronize()
+    ref, _ = oracle.run_batch(b)
+    U.compare(out, ref, dtype, f"append/{W}/{Hkv}/s{splits}")
+    iv = torch.int16 if dtype == "bf16" else torch.int32
+    assert torch.equal(d.k.cpu().view(iv), b.k_cache.view(iv))
+    assert torch.equal(d.v.cpu().view(iv), b.v_cache.view(iv))
+    # The plain decode on the updated cache gives the same bits.
+    out2 = U.decode(d, splits=splits)
+    assert torch.equal(out.view(iv), out2.view(iv))
+
+
 def test_decode_deterministic():
     b = _mk(41, [3000, 5000], [1, 1], Hq=48, Hkv=8, W=0, R=8192)
     d = U.Dev(b)
