@@ -155,8 +155,8 @@ def main():
     ap.add_argument("--batch", type=int, default=0,
                     help="sequences in a decode workload (0 = the workload's own)")
     ap.add_argument("--append", action="store_true",
-                    help="decode workloads: inkling_rel_attn_decode_append (the step's K/V "
-                         "rows stored into the cache in the same launch)")
+                    help="the *_append entry points: the step's new K/V rows are stored "
+                         "into the cache in the same launch")
     ap.add_argument("--graph", action="store_true",
                     help="capture each replica's step once in a HIP graph and time replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -220,14 +220,11 @@ def main():
         f"D={batch.head_dim} W={batch.window} R={batch.rel_len}")
     parts = list(inputs.split_mixed(batch)) if split_mixed else [batch]
     parts = [p for p in parts if p.num_seqs > 0]
-    if args.append and not wl.endswith("decode"):
-        log("--append applies to the decode workloads only")
-        sys.exit(2)
     alg = [algorithmic(p) for p in parts]
     step_bytes = sum(a["bytes"] for a in alg)
     if args.append:
         # k_new and v_new read once, and the same rows written to the cache.
-        step_bytes += 2 * 2 * batch.num_seqs * batch.num_kv_heads * batch.head_dim * (
+        step_bytes += 2 * 2 * batch.total_q * batch.num_kv_heads * batch.head_dim * (
             2 if batch.dtype == "bf16" else 4)
     step_flops = sum(a["flops"] for a in alg)
     replicas = args.replicas or max(2, math.ceil(2 * MALL_BYTES / step_bytes) + 1)
@@ -275,7 +272,17 @@ def main():
                 a, dims = binding.prefill_args(q, k, v, bt, sl, cu, rel, p.window, p.scale,
                                                out, max_q_len=p.max_q_len,
                                                max_seq_len=p.max_seq_len, stream=launch_stream)
-                rc.append(("inkling_rel_attn_prefill", a))
+                if args.append:
+                    # The new tokens' rows are the ones already at their keys.
+                    rows = [(i, pos) for i in range(p.num_seqs)
+                            for pos in range(int(p.seq_lens[i]) - int(p.q_lens[i]),
+                                             int(p.seq_lens[i]))]
+                    kn = torch.stack([p.k_logical[i][pos] for i, pos in rows]).to(dev)
+                    vn = torch.stack([p.v_logical[i][pos] for i, pos in rows]).to(dev)
+                    a = a[:1] + (binding._ptr(kn), binding._ptr(vn)) + a[1:]
+                    keep += [kn, vn]
+                rc.append(("inkling_rel_attn_prefill_append" if args.append
+                           else "inkling_rel_attn_prefill", a))
                 keep += [q, k, v, rel, bt, sl, cu, out, dims]
         calls.append(rc)
     torch.cuda.synchronize()

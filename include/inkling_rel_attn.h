@@ -105,6 +105,31 @@ inkling_status_t inkling_rel_attn_prefill(
     void* stream /* hipStream_t; NULL = default stream */);
 
 /*
+ * Prefill that also appends the new tokens' K/V rows to the cache, in the
+ * same launch (the attention-side KV write of the TensorRT-LLM Inkling
+ * page's pull request, commit list: the attention op's arguments include
+ * a switch to skip its own KV write).  Same inputs, outputs and errors as
+ * inkling_rel_attn_prefill, plus:
+ *   k_new, v_new  [total_q, Hkv, head_dim] in the cache dtype, rows aligned
+ *                 with q: row cu_q_lens[b] + t holds the K / V of token t
+ *                 of sequence b, at position L_b - n_b + t.  Each row is
+ *                 stored into its cache slot (page block_table[b][pos / 16],
+ *                 slot pos % 16), and the attention reads every new key
+ *                 from these rows, whatever the slots held before.
+ *   k_cache, v_cache  read and written; slots of new tokens must be
+ *                 distinct across the batch; k_new / v_new must not
+ *                 overlap the caches.
+ * Null k_new or v_new (with total_q > 0) is INKLING_ERR_INVALID_ARGUMENT.
+ * Later work on the stream sees the stored rows.
+ */
+inkling_status_t inkling_rel_attn_prefill_append(
+    const void* q, const void* k_new, const void* v_new, void* k_cache,
+    void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+    const int32_t* cu_q_lens, const void* rel_logits, int32_t window,
+    float scale, void* out, const inkling_rel_attn_dims_t* dims,
+    void* stream);
+
+/*
  * Single-token decode with split-KV (vLLM page, section "Changes": the keys
  * of each sequence are split into num_splits parts, each part produces a
  * partial output and its log-sum-exp, and a merge pass combines them).

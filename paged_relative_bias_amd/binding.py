@@ -23,6 +23,7 @@ OK = 0
 DTYPE_BF16, DTYPE_FP32 = 0, 1
 SYMBOLS = (
     "inkling_rel_attn_prefill",
+    "inkling_rel_attn_prefill_append",
     "inkling_rel_attn_decode",
     "inkling_rel_attn_decode_append",
     "inkling_rel_attn_num_splits",
@@ -61,6 +62,8 @@ def load(path: str = LIB_PATH):
     DP = ctypes.POINTER(Dims)
     lib.inkling_rel_attn_prefill.restype = ctypes.c_int
     lib.inkling_rel_attn_prefill.argtypes = [P, P, P, P, P, P, P, I32, F32, P, DP, P]
+    lib.inkling_rel_attn_prefill_append.restype = ctypes.c_int
+    lib.inkling_rel_attn_prefill_append.argtypes = [P, P, P, P, P, P, P, P, P, I32, F32, P, DP, P]
     lib.inkling_rel_attn_decode.restype = ctypes.c_int
     lib.inkling_rel_attn_decode.argtypes = [P, P, P, P, P, P, I32, F32, I32, P,
                                             ctypes.c_size_t, P, DP, P]
@@ -147,6 +150,22 @@ def prefill(q, k_cache, v_cache, block_table, seq_lens, cu_q_lens, rel_logits,
         float(scale), _ptr(out), ctypes.byref(dims), _stream(stream))
     if st != OK:
         raise InklingError(st, "inkling_rel_attn_prefill")
+
+
+def prefill_append(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens, cu_q_lens,
+                   rel_logits, window: int, scale: float, out, *, max_q_len: int,
+                   max_seq_len: int, stream=None) -> None:
+    """inkling_rel_attn_prefill_append on device tensors: prefill that also
+    stores the new tokens' k_new / v_new rows ([total_q, Hkv, D])."""
+    dims = dims_for(q, k_cache, block_table, rel_logits,
+                    num_seqs=seq_lens.shape[0], max_q_len=max_q_len,
+                    max_seq_len=max_seq_len)
+    st = load().inkling_rel_attn_prefill_append(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+        _ptr(block_table), _ptr(seq_lens), _ptr(cu_q_lens), _ptr(rel_logits),
+        int(window), float(scale), _ptr(out), ctypes.byref(dims), _stream(stream))
+    if st != OK:
+        raise InklingError(st, "inkling_rel_attn_prefill_append")
 
 
 def num_splits(dims: Dims, window: int, device: int = 0) -> int:

@@ -160,11 +160,16 @@ size_t inkling_rel_attn_decode_workspace_bytes(const inkling_rel_attn_dims_t* di
   return workspace_for(dims, num_splits);
 }
 
-inkling_status_t inkling_rel_attn_prefill(const void* q, const void* k_cache, const void* v_cache,
-                                          const int32_t* block_table, const int32_t* seq_lens,
-                                          const int32_t* cu_q_lens, const void* rel_logits,
-                                          int32_t window, float scale, void* out,
-                                          const inkling_rel_attn_dims_t* dims, void* stream) {
+}  // extern "C"
+
+namespace {
+
+inkling_status_t prefill_impl(const void* q, const void* k_new, const void* v_new,
+                              const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* seq_lens,
+                              const int32_t* cu_q_lens, const void* rel_logits, int32_t window,
+                              float scale, void* out, const inkling_rel_attn_dims_t* dims,
+                              void* stream) {
   inkling_status_t st = check_dims(dims);
   if (st != INKLING_OK) return st;
   if (!std::isfinite(scale)) return INKLING_ERR_INVALID_ARGUMENT;
@@ -181,6 +186,8 @@ inkling_status_t inkling_rel_attn_prefill(const void* q, const void* k_cache, co
   p.cu_q_lens = cu_q_lens;
   p.rel = rel_logits;
   p.out = out;
+  p.k_new = k_new;
+  p.v_new = v_new;
   p.hq = dims->num_q_heads;
   p.hkv = dims->num_kv_heads;
   p.group = dims->num_q_heads / dims->num_kv_heads;
@@ -218,9 +225,6 @@ inkling_status_t inkling_rel_attn_prefill(const void* q, const void* k_cache, co
   return e == hipSuccess ? INKLING_OK : INKLING_ERR_LAUNCH;
 }
 
-}  // extern "C"
-
-namespace {
 
 inkling_status_t decode_impl(const void* q, const void* k_new, const void* v_new,
                              const void* k_cache, const void* v_cache,
@@ -321,6 +325,26 @@ inkling_status_t decode_impl(const void* q, const void* k_new, const void* v_new
 }  // namespace
 
 extern "C" {
+
+inkling_status_t inkling_rel_attn_prefill(const void* q, const void* k_cache, const void* v_cache,
+                                          const int32_t* block_table, const int32_t* seq_lens,
+                                          const int32_t* cu_q_lens, const void* rel_logits,
+                                          int32_t window, float scale, void* out,
+                                          const inkling_rel_attn_dims_t* dims, void* stream) {
+  return prefill_impl(q, nullptr, nullptr, k_cache, v_cache, block_table, seq_lens, cu_q_lens,
+                      rel_logits, window, scale, out, dims, stream);
+}
+
+inkling_status_t inkling_rel_attn_prefill_append(
+    const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+    const int32_t* block_table, const int32_t* seq_lens, const int32_t* cu_q_lens,
+    const void* rel_logits, int32_t window, float scale, void* out,
+    const inkling_rel_attn_dims_t* dims, void* stream) {
+  if (dims != nullptr && dims->total_q > 0 && (k_new == nullptr || v_new == nullptr))
+    return INKLING_ERR_INVALID_ARGUMENT;
+  return prefill_impl(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens, cu_q_lens,
+                      rel_logits, window, scale, out, dims, stream);
+}
 
 inkling_status_t inkling_rel_attn_decode(const void* q, const void* k_cache, const void* v_cache,
                                          const int32_t* block_table, const int32_t* seq_lens,

@@ -86,6 +86,9 @@ __device__ __forceinline__ uint32_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t o
 __device__ __forceinline__ uint32_t sgpr_u32(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_readfirstlane((int)x);
 }
+__device__ __forceinline__ uint64_t sgpr_u64(uint64_t x) {
+  return (uint64_t)sgpr_u32((uint32_t)x) | ((uint64_t)sgpr_u32((uint32_t)(x >> 32)) << 32);
+}
 
 __device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
 __device__ __forceinline__ int imax(int a, int b) { return a > b ? a : b; }

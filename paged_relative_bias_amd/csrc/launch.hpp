@@ -30,6 +30,8 @@ struct PrefillParams {
   const int32_t* cu_q_lens;
   const void* rel;
   void* out;
+  const void* k_new;  // [total_q, Hkv, D] rows of the new tokens (keys L - n ..
+  const void* v_new;  //   L - 1), stored into the cache and used (null: none)
   int32_t hq, hkv, group;
   int32_t num_blocks, max_blocks, rel_len, window, total_q;
   int32_t bq;         // query tokens per workgroup

@@ -93,7 +93,10 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <typename T, int D>
+// APPEND: the new tokens' K/V rows come from P.k_new / P.v_new and are
+// stored into the cache (a separate instantiation, so the plain kernel's
+// loads stay free of control flow).
+template <typename T, int D, bool APPEND>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_kernel(const PrefillParams P) {
   using C = Prefill<T, D>;
@@ -186,6 +189,12 @@ prefill_kernel(const PrefillParams P) {
   const uint32_t head_bytes = (uint32_t)g * D * SZ;
   const char* kg = static_cast<const char*>(P.k);
   const char* vg = static_cast<const char*>(P.v);
+  // Append: the new tokens' rows (keys pbase .. je - 1) are read from
+  // k_new / v_new, never from the cache, and each workgroup stores its own
+  // tokens' rows into the cache, so no workgroup waits for another's store.
+  constexpr bool app = APPEND;
+  const uint64_t kn = reinterpret_cast<uint64_t>(P.k_new);
+  const uint64_t vn = reinterpret_cast<uint64_t>(P.v_new);
   // Bias rows of tokens [t0, tend), all heads: row (t, h') at
   // ((t - t0) * Hq + h') * R.
   const __amdgpu_buffer_rsrc_t rel_rsrc =
@@ -231,13 +240,25 @@ prefill_kernel(const PrefillParams P) {
       const int pgi = iclamp((key0 >> 4) - pg_lo, 0, P.pid_cap - 1);
       const uint64_t page = (uint32_t)__builtin_amdgcn_readfirstlane(pid_lds[pgi]);
       const uint32_t nrec = sgpr_u32((uint32_t)iclamp(je - (key0 & ~15), 0, 16) * slot_bytes);
-      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + page * page_bytes, nrec);
-      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + page * page_bytes, nrec);
+      // With an append, slot s of this page is new token (key0 & ~15) + s -
+      // pbase: the new rows are addressed like a page whose base sits
+      // (key0 & ~15) - pbase rows from k_new's token q0 (only slots of new
+      // tokens are ever read through it).
+      const uint64_t new_off =
+          (uint64_t)((int64_t)(q0 + (key0 & ~15) - pbase) * (int64_t)slot_bytes);
+      const bool all_new = app && key0 >= pbase;         // wave-uniform
+      const uint64_t kb =
+          sgpr_u64(all_new ? kn + new_off : reinterpret_cast<uint64_t>(kg) + page * page_bytes);
+      const uint64_t vb =
+          sgpr_u64(all_new ? vn + new_off : reinterpret_cast<uint64_t>(vg) + page * page_bytes);
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const void*>(kb), nrec);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const void*>(vb), nrec);
 #pragma unroll
       for (int i = 0; i < C::LPT; ++i) {
         rg.kv[i] = bload128(rk, kv_lane[i]);
         rg.kv[C::LPT + i] = bload128(rv, kv_lane[i]);
       }
+
     }
     const bool wtile = wact && kt < wje && kt + N > wjb;  // wave-uniform
 #pragma unroll
@@ -249,7 +270,8 @@ prefill_kernel(const PrefillParams P) {
       rg.b[i] = bload128(rel_rsrc, wtile ? off : kOOB);
     }
   };
-  auto commit = [&](const Regs& rg, int st) {
+  // Tile kt's loads into LDS stage st.
+  auto commit = [&](const Regs& rg, int st, int kt) {
     T* Ks = stage(st);
     T* Vs = Ks + N * KP;
 #pragma unroll
@@ -258,6 +280,33 @@ prefill_kernel(const PrefillParams P) {
       const int chunk = (lane % CPR) * VEC;
       *reinterpret_cast<uint4*>(Ks + key * KP + chunk) = rg.kv[i];
       *reinterpret_cast<uint4*>(Vs + key * VP + chunk) = rg.kv[C::LPT + i];
+    }
+    if constexpr (APPEND) {
+      const int key0 = kt + C::KW * wave;                 // wave-uniform
+      if (key0 < pbase && key0 + C::KW > pbase) {         // rare
+        // The wave's keys cross the first new token: the rows staged above
+        // for its new keys came from the cache; replace them with the new
+        // rows.
+        const uint64_t new_off =
+            (uint64_t)((int64_t)(q0 + (key0 & ~15) - pbase) * (int64_t)slot_bytes);
+        const uint32_t nrec = sgpr_u32((uint32_t)iclamp(je - (key0 & ~15), 0, 16) * slot_bytes);
+        const __amdgpu_buffer_rsrc_t nk =
+            make_rsrc(reinterpret_cast<const void*>(sgpr_u64(kn + new_off)), nrec);
+        const __amdgpu_buffer_rsrc_t nv =
+            make_rsrc(reinterpret_cast<const void*>(sgpr_u64(vn + new_off)), nrec);
+#pragma unroll
+        for (int i = 0; i < C::LPT; ++i) {
+          const int key = C::KW * wave + KPI * i + lane / CPR;
+          const int chunk = (lane % CPR) * VEC;
+          const bool isnew = kt + key >= pbase;
+          const uint4 a = bload128(nk, isnew ? kv_lane[i] : kOOB);
+          const uint4 c = bload128(nv, isnew ? kv_lane[i] : kOOB);
+          if (isnew) {
+            *reinterpret_cast<uint4*>(Ks + key * KP + chunk) = a;
+            *reinterpret_cast<uint4*>(Vs + key * VP + chunk) = c;
+          }
+        }
+      }
     }
     unsigned char* Bw = bias_lds + (size_t)(wave * 2 + st) * 32 * sbp;
 #pragma unroll
@@ -417,24 +466,41 @@ prefill_kernel(const PrefillParams P) {
   // is computed and goes to the other stage after.  (A second buffer, for
   // a tile more in flight, measured no faster and costs 28 VGPRs.)  Loads
   // past the last tile read nothing, so no load sits under control flow.
+  if (app) {                                             // uniform
+    // Store this workgroup's tokens' new K/V rows of head g into the cache.
+    lds_barrier();                                       // page ids ready
+    const int chunks = (tend - t0) * 2 * CPR;
+    for (int c = tid; c < chunks; c += blockDim.x) {
+      const int t = t0 + c / (2 * CPR), r = c % (2 * CPR);
+      const bool isv = r >= CPR;
+      const int ch = isv ? r - CPR : r;
+      const int key = pbase + t;
+      const uint64_t page = (uint32_t)pid_lds[(key >> 4) - pg_lo];
+      const uint64_t dst = page * page_bytes + (uint64_t)(key & 15) * slot_bytes + head_bytes +
+                           (uint64_t)ch * 16u;
+      const uint64_t src = ((uint64_t)(q0 + t) * P.hkv + g) * D * SZ + (uint64_t)ch * 16u;
+      const uint4 v = *reinterpret_cast<const uint4*>((isv ? vn : kn) + src);
+      *reinterpret_cast<uint4*>(reinterpret_cast<char*>(const_cast<void*>(isv ? P.v : P.k)) + dst) = v;
+    }
+  }
   Regs ra;
   while (true) {
     lds_barrier();                                       // page ids ready
     int kt = jb & ~15;
     issue(ra, kt);
-    commit(ra, 0);
+    commit(ra, 0, kt);
     lds_barrier();
     while (true) {
       issue(ra, kt + N);
       compute(kt, 0);
       if (kt + N >= je) break;                           // workgroup-uniform
-      commit(ra, 1);
+      commit(ra, 1, kt + N);
       lds_barrier();
       kt += N;
       issue(ra, kt + N);
       compute(kt, 1);
       if (kt + N >= je) break;
-      commit(ra, 0);
+      commit(ra, 0, kt + N);
       lds_barrier();
       kt += N;
     }
@@ -472,20 +538,26 @@ size_t lds_bytes_t(int waves, int sb_pitch, int pid_cap) {
          (size_t)pid_cap * 4 + (size_t)kPrefillWaves * 4;
 }
 
-template <typename T, int D>
-hipError_t launch_t(const PrefillParams& p, hipStream_t stream) {
+template <typename T, int D, bool APPEND>
+hipError_t launch_a(const PrefillParams& p, hipStream_t stream) {
   const size_t lds = lds_bytes_t<T, D>(kPrefillWaves, p.sb_pitch, p.pid_cap);
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<T, D>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&prefill_kernel<T, D, APPEND>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int64_t total = (int64_t)p.nqb * p.num_seqs * p.hkv;
   const int64_t grid = ((total + 7) / 8) * 8;
-  prefill_kernel<T, D><<<dim3((unsigned)grid), dim3(kPrefillWaves * 64), lds, stream>>>(p);
+  prefill_kernel<T, D, APPEND><<<dim3((unsigned)grid), dim3(kPrefillWaves * 64), lds, stream>>>(p);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_t(const PrefillParams& p, hipStream_t stream) {
+  return p.k_new != nullptr ? launch_a<T, D, true>(p, stream) : launch_a<T, D, false>(p, stream);
 }
 
 }  // namespace

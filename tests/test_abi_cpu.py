@@ -119,6 +119,14 @@ def test_decode_append_needs_new_rows():
     assert st == 1   # INKLING_ERR_INVALID_ARGUMENT
 
 
+def test_prefill_append_needs_new_rows():
+    d = _dims(num_seqs=2, total_q=100, max_q_len=50)
+    st = B.load().inkling_rel_attn_prefill_append(
+        None, None, None, None, None, None, None, None, None, 512, 1.0, None,
+        ctypes.byref(d), None)
+    assert st == 1   # INKLING_ERR_INVALID_ARGUMENT
+
+
 def test_split_heuristic_bounds():
     # 64 x 16 units already give four per compute unit on 256 CUs.
     assert B.num_splits(_dims(num_seqs=64, total_q=64), 512, -1) == 1

@@ -86,6 +86,44 @@ def test_prefill_matches_oracle(case):
     U.compare(out, ref, dtype, name)
 
 
+@pytest.mark.parametrize("name,L,n,Hq,Hkv,D,W,R,dtype", [
+    ("empty_cache_local", [700, 333, 40], [700, 333, 40], 48, 16, 128, 512, 512, "bf16"),
+    ("cached_prefix_unaligned", [900, 533, 77], [130, 509, 70], 12, 4, 128, 256, 256, "bf16"),
+    ("global_mixed_rows", [1500, 77, 800, 1], [1, 77, 300, 1], 48, 8, 128, 0, 8192, "bf16"),
+    ("fp32", [150, 37], [45, 37], 8, 4, 64, 40, 40, "fp32"),
+])
+def test_prefill_append(name, L, n, Hq, Hkv, D, W, R, dtype):
+    """Prefill with the new tokens' K/V stored in the same launch: their
+    cache slots hold NaN beforehand, the output must match the oracle on
+    the intended cache, and afterwards the whole cache must equal it bit
+    for bit.  Cached prefixes that end inside a page make a wave's keys
+    cross the first new token."""
+    b = _mk(70 + len(name), L, n, Hq=Hq, Hkv=Hkv, D=D, W=W, R=R, dtype=dtype)
+    rows_k, rows_v = [], []
+    d = U.Dev(b)
+    for i, (l, m) in enumerate(zip(L, n)):
+        for pos in range(l - m, l):
+            rows_k.append(b.k_logical[i][pos])
+            rows_v.append(b.v_logical[i][pos])
+            page = int(b.block_table[i, pos // 16])
+            d.k[page, pos % 16] = float("nan")
+            d.v[page, pos % 16] = float("nan")
+    k_new = torch.stack(rows_k).contiguous().cuda()
+    v_new = torch.stack(rows_v).contiguous().cuda()
+    out = torch.full_like(d.q, float("nan"))
+    _say(f"prefill append {name}: L={L} n={n} Hkv={Hkv} W={W} {dtype}")
+    binding.prefill_append(d.q, k_new, v_new, d.k, d.v, d.bt, d.sl, d.cu, d.rel, b.window,
+                           b.scale, out, max_q_len=b.max_q_len, max_seq_len=b.max_seq_len)
+    torch.cuda.synchronize()
+    ref, _ = oracle.run_batch(b)
+    U.compare(out, ref, dtype, f"prefill_append/{name}")
+    iv = torch.int16 if dtype == "bf16" else torch.int32
+    assert torch.equal(d.k.cpu().view(iv), b.k_cache.view(iv))
+    assert torch.equal(d.v.cpu().view(iv), b.v_cache.view(iv))
+    # The plain prefill on the updated cache gives the same bits.
+    assert torch.equal(out.view(iv), U.prefill(d).view(iv))
+
+
 def test_prefill_deterministic_and_page_permutation_bitexact():
     b = _mk(20, [600, 211], [600, 211], Hq=12, Hkv=4, W=128, R=128)
     _say("prefill determinism / page permutation")
