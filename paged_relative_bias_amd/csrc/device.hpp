@@ -26,7 +26,9 @@ __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // 
 template <>
 __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 
-// 2^x on the transcendental unit; callers only pass x <= 0 or -inf.
+// 2^x on the transcendental unit.  Callers pass -inf (giving 0) or x below
+// about 58 (a logit at most kOver = 40 natural units above its softmax
+// reference), far from overflow.
 __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);
 }

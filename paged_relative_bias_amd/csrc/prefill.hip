@@ -11,8 +11,10 @@
 // XCDs receives a contiguous run of work, i.e. consecutive query blocks of
 // one (b, g), whose key ranges overlap, share that XCD's L2.  The MFMA
 // columns of a workgroup are its (query head in group, token) pairs,
-// head-major (column c: head g*G + c / bq, token t0 + c % bq); each wave
-// owns 32 columns.
+// token-major (column c: head g*G + c % G, token t0 + c / G); each wave
+// owns 32 columns, i.e. about 32 / G consecutive tokens of every head, so
+// its visible key range is narrow (and the rows of a short sequence, such
+// as a decode row, fill the first waves only).
 //
 // Key tiles of 32 keys sweep the union of the block's visible ranges,
 // double-buffered in LDS:
@@ -135,17 +137,15 @@ prefill_kernel(const PrefillParams P) {
   // This lane's column (query head, token).
   const int col = lane & 31, u = lane >> 5;
   const int wc = wave * 32 + col;
-  const int hh = wc / bq;
-  const int tc = t0 + wc % bq;
+  const int hh = wc % G;
+  const int tc = t0 + wc / G;
   const bool cval = hh < G && tc < tend;
   const int h = g * G + (hh < G ? hh : 0);
   const int pc = pbase + tc;
-  // The wave's token range (a wave may straddle two heads, then it covers
-  // every token of the block) and its visible key range.
+  // The wave's token range and its visible key range.
   const int c_lo = wave * 32, c_hi = imin(c_lo + 31, G * bq - 1);
-  const bool one_head = c_lo / bq == c_hi / bq;
-  const int wt_lo = one_head ? t0 + c_lo % bq : t0;
-  const int wt_hi = imin(one_head ? t0 + c_hi % bq + 1 : t0 + bq, tend);   // exclusive
+  const int wt_lo = t0 + c_lo / G;
+  const int wt_hi = imin(t0 + c_hi / G + 1, tend);   // exclusive
   const bool wact = c_lo < G * bq && wt_lo < tend;
   const int wjb = W > 0 ? imax(0, pbase + wt_lo - W + 1) : 0;
   const int wje = pbase + wt_hi;
@@ -224,7 +224,7 @@ prefill_kernel(const PrefillParams P) {
     const int c = i * 64 + lane;
     const int r = c / sbc, part = c - r * sbc;
     const int rc = wave * 32 + r;
-    const int rh = rc / bq, rt = t0 + rc % bq;
+    const int rh = rc % G, rt = t0 + rc / G;
     const bool ok = r < 32 && rh < G && rt < tend;
     b_row[i] = ((uint32_t)((rt - t0) * hq + g * G + rh) * (uint32_t)R + (uint32_t)(part * VEC)) * SZ |
                (ok ? 0u : kOOB);
