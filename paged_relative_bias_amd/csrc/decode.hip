@@ -388,7 +388,7 @@ decode_kernel(const DecodeParams P) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int j = kt + 16 * (i >> 2) + 4 * u4 + (i & 3);
-        x[i] = (j >= v_lo && j < s_hi) ? x[i] : kNegInf;
+        x[i] = (uint32_t)(j - v_lo) < (uint32_t)(s_hi - v_lo) ? x[i] : kNegInf;
       }
     }
     const float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),

@@ -110,6 +110,9 @@ prefill_kernel(const PrefillParams P) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   constexpr int nw = kPrefillWaves;
   const int G = P.group, bq = P.bq, R = P.rel_len, SB = P.sb, W = P.window;
+  // A key at distance d is visible when 0 <= d < W (any d >= 0 without a
+  // window): one unsigned compare against wlim.
+  const uint32_t wlim = W > 0 ? (uint32_t)W : 0x80000000u;
   const int64_t hq = P.hq;
 
   // XCD-aware work index: workgroup id x runs on XCD x % 8; give each XCD
@@ -382,7 +385,7 @@ prefill_kernel(const PrefillParams P) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int d = D0 - (8 * (i >> 2) + (i & 3));
-          const bool vis = d >= 0 && (W <= 0 || d < W);
+          const bool vis = (uint32_t)d < wlim;            // 0 <= d < window
           x[i] = vis ? x[i] : kNegInf;
         }
       }
@@ -393,7 +396,7 @@ prefill_kernel(const PrefillParams P) {
         // di is always inside the staged run, so the read is unconditional.
         const int di = iclamp(imin(d, R - 1) - base_c, 0, SB - 1);
         const float bv = to_f32(brow[di]);
-        const bool vis = d >= 0 && (W <= 0 || d < W);
+        const bool vis = (uint32_t)d < wlim;
         x[i] = vis ? fmaf(s[i], P.scale, bv) : kNegInf;
       }
     }
