@@ -335,6 +335,37 @@ def test_full_long_global_decode():
 
 
 @pytest.mark.timeout(400)
+def test_long_context_prefill_sampled():
+    """A 512-token chunk on top of ~150K cached keys (global layer, R =
+    8192, so the clamp is active for most keys) and a short sequence: the
+    page-id table holds ~9.4K entries.  Sampled rows against the oracle,
+    plus the fused-append variant on the same batch."""
+    L = [150_000 + 512, 700]
+    n = [512, 700]
+    b = _mk(80, L, n, Hq=12, Hkv=2, W=0, R=8192)
+    _say(f"long-context prefill L={L} n={n}")
+    d = U.Dev(b)
+    out = U.prefill(d)
+    rows = U.sample_rows(b, 600, seed=4)
+    ref = U.oracle_rows(b, rows)
+    U.compare(out, ref, "bf16", "long_prefill", rows=rows)
+    # Fused append: the chunk's K/V rows come in beside the call (their
+    # slots NaN beforehand); the output must not change.
+    k_new = torch.cat([b.k_logical[i][l - m:l] for i, (l, m) in enumerate(zip(L, n))]).cuda()
+    v_new = torch.cat([b.v_logical[i][l - m:l] for i, (l, m) in enumerate(zip(L, n))]).cuda()
+    for i, (l, m) in enumerate(zip(L, n)):
+        for pos in range(l - m, l):
+            page = int(b.block_table[i, pos // 16])
+            d.k[page, pos % 16] = float("nan")
+            d.v[page, pos % 16] = float("nan")
+    out2 = torch.full_like(d.q, float("nan"))
+    binding.prefill_append(d.q, k_new, v_new, d.k, d.v, d.bt, d.sl, d.cu, d.rel, b.window,
+                           b.scale, out2, max_q_len=b.max_q_len, max_seq_len=b.max_seq_len)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+@pytest.mark.timeout(400)
 def test_full_local_prefill_sampled():
     b = _full("local_prefill")
     _say("full local_prefill (sampled rows)")
