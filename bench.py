@@ -54,8 +54,10 @@ def algorithmic(batch):
     Per sequence b with query positions [L_b - n_b, L_b):
       keys_read_b  = keys visible to at least one of its queries
       pairs_b      = sum over its queries of visible keys (per head)
+      entries_b    = sum over its queries of distinct bias entries read,
+                     min(visible keys, R) (distances >= R - 1 share entry R - 1)
     bytes = sum_b keys_read_b * Hkv * D * e * 2     (K and V, once per KV head)
-          + sum_b pairs_b * Hq * e                  (bias entries used)
+          + sum_b entries_b * Hq * e                (bias entries used)
           + total_q * Hq * D * e * 2                (q in, out)
           + 4 * sum_b ceil(L_b / 16)-pages touched  (block table)
     flops = 4 * D * Hq * sum_b pairs_b              (QK^T and PV)
@@ -63,8 +65,9 @@ def algorithmic(batch):
     """
     e = 2 if batch.dtype == "bf16" else 4
     Hq, Hkv, D, W = batch.num_q_heads, batch.num_kv_heads, batch.head_dim, batch.window
+    R = batch.rel_len
     kv = bias = pages = 0
-    pairs = 0
+    pairs = entries = 0
     for b in range(batch.num_seqs):
         n, L = int(batch.q_lens[b]), int(batch.seq_lens[b])
         if n == 0:
@@ -72,11 +75,12 @@ def algorithmic(batch):
         p = np.arange(L - n, L, dtype=np.int64)
         vis = np.minimum(p + 1, W) if W > 0 else p + 1
         pairs += int(vis.sum())
+        entries += int(np.minimum(vis, R).sum())
         lo = max(0, L - n - W + 1) if W > 0 else 0
         keys = L - lo
         kv += keys * Hkv * D * e * 2
         pages += (L - 1) // 16 - lo // 16 + 1
-    bias = pairs * Hq * e
+    bias = entries * Hq * e
     qo = batch.total_q * Hq * D * e * 2
     total = kv + bias + qo + 4 * pages
     return {"bytes": total, "kv": kv, "bias": bias, "qo": qo,
