@@ -29,6 +29,8 @@
  *    library never allocates, frees, copies between host and device or
  *    synchronises; all work is enqueued on `stream` (graph-capturable).
  *  - q, k_cache, v_cache, rel_logits and out share one dtype (dims->dtype).
+ *    Every tensor pointer (and the decode workspace) is 16-byte aligned;
+ *    a misaligned one is INKLING_ERR_INVALID_ARGUMENT.
  *  - k_cache / v_cache: [num_blocks, block_size, Hkv, head_dim]; logical key
  *    j of sequence b lives in page block_table[b * max_blocks_per_seq + j /
  *    block_size], slot j % block_size.

@@ -9,6 +9,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <initializer_list>
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
@@ -84,6 +85,14 @@ int32_t splits_for(const inkling_rel_attn_dims_t* d, int32_t window, int cus) {
   int64_t s = std::min<int64_t>(want, cap);
   s = std::max<int64_t>(1, std::min<int64_t>(s, kMaxSplits));
   return (int32_t)s;
+}
+
+// Tensors are read and written in 16-byte vectors.
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+bool all_aligned16(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p != nullptr && !aligned16(p)) return false;
+  return true;
 }
 
 size_t workspace_for(const inkling_rel_attn_dims_t* d, int32_t splits) {
@@ -176,6 +185,8 @@ inkling_status_t prefill_impl(const void* q, const void* k_new, const void* v_ne
   if (dims->num_seqs == 0 || dims->total_q == 0 || dims->max_q_len == 0) return INKLING_OK;
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !cu_q_lens || !rel_logits || !out)
     return INKLING_ERR_INVALID_ARGUMENT;
+  if (!all_aligned16({q, k_cache, v_cache, rel_logits, out, k_new, v_new}))
+    return INKLING_ERR_INVALID_ARGUMENT;
 
   PrefillParams p{};
   p.q = q;
@@ -239,6 +250,8 @@ inkling_status_t decode_impl(const void* q, const void* k_new, const void* v_new
   if (dims->total_q != dims->num_seqs) return INKLING_ERR_INVALID_ARGUMENT;
   if (dims->num_seqs == 0) return INKLING_OK;
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !rel_logits || !out)
+    return INKLING_ERR_INVALID_ARGUMENT;
+  if (!all_aligned16({q, k_cache, v_cache, rel_logits, out, k_new, v_new}))
     return INKLING_ERR_INVALID_ARGUMENT;
   int dev = 0;
   if (num_splits == 0) {

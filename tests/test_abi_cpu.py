@@ -110,6 +110,17 @@ def test_workspace_size_formula():
     assert B.decode_workspace_bytes(d, 0, 129) == 0
 
 
+def test_misaligned_tensor_is_rejected():
+    d = _dims(num_seqs=2, total_q=2)
+    odd = ctypes.c_void_p(0x1002)
+    st = B.load().inkling_rel_attn_prefill(odd, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 512, 0.1,
+                                           FAKE, ctypes.byref(d), None)
+    assert st == 1   # INKLING_ERR_INVALID_ARGUMENT
+    st = B.load().inkling_rel_attn_decode(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 512, 0.1, 1, None,
+                                          0, odd, ctypes.byref(d), None)
+    assert st == 1
+
+
 def test_decode_append_needs_new_rows():
     # Rejected before any device work: null k_new / v_new.
     d = _dims(num_seqs=4, total_q=4)
