@@ -348,6 +348,16 @@ prefill_kernel(const PrefillParams P) {
     const T* brow = reinterpret_cast<const T*>(bias_lds + (size_t)(wave * 2 + st) * 32 * sbp +
                                                col * sbp);
     const int base_c = iclamp(floor_to(pc - kt - (N - 1), VEC), 0, R - SB);
+    const int D0 = pc - kt - 4 * u;
+    // Bias runs of the fast path, read before the QK product so that their
+    // LDS latency overlaps it (in-bounds for every lane; unused on the
+    // general path).
+    uint2 brun[4];
+    if constexpr (C::kBF16) {
+      const T* bb = brow + imin(D0 - base_c - 27, SB - 28);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) __builtin_memcpy(&brun[k], bb + 24 - 8 * k, 8);
+    }
     f32x16 s = f32x16{};
     if constexpr (C::kBF16) {
       const bf16* krow = Ks + col * KP + 8 * u;
@@ -370,17 +380,28 @@ prefill_kernel(const PrefillParams P) {
     // Tiles with no distance at the clamp read the run directly and mask by
     // select (only on tiles that cross the window or causal boundary);
     // tiles that reach the clamp take the general path.
-    const int D0 = pc - kt - 4 * u;
     const bool unclamped = (wje - 1) - kt <= R - 1;       // wave-uniform
     const bool full = (W <= 0 || (wje - 1) - kt < W) && (pbase + wt_lo) - (kt + N - 1) >= 0;
     if (unclamped) {
       // Entries start .. start + 27 of the staged run; for real columns
       // start + 27 <= SB - 1 on these tiles, and the bound keeps padding
       // columns' reads inside the staging area as well.
-      const T* bb = brow + imin(D0 - base_c - 27, SB - 28);
+      if constexpr (C::kBF16) {
+        // Run k holds entries 24 - 8k .. 27 - 8k; x[4k + j] takes entry
+        // 27 - 8k - j.
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        x[i] = fmaf(s[i], P.scale, to_f32(bb[27 - (8 * (i >> 2) + (i & 3))]));
+        for (int k = 0; k < 4; ++k) {
+          x[4 * k + 0] = fmaf(s[4 * k + 0], P.scale, __builtin_bit_cast(float, brun[k].y & 0xffff0000u));
+          x[4 * k + 1] = fmaf(s[4 * k + 1], P.scale, __builtin_bit_cast(float, brun[k].y << 16));
+          x[4 * k + 2] = fmaf(s[4 * k + 2], P.scale, __builtin_bit_cast(float, brun[k].x & 0xffff0000u));
+          x[4 * k + 3] = fmaf(s[4 * k + 3], P.scale, __builtin_bit_cast(float, brun[k].x << 16));
+        }
+      } else {
+        const T* bb = brow + imin(D0 - base_c - 27, SB - 28);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          x[i] = fmaf(s[i], P.scale, to_f32(bb[27 - (8 * (i >> 2) + (i & 3))]));
+      }
       if (!full) {                                        // wave-uniform
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -417,14 +438,22 @@ prefill_kernel(const PrefillParams P) {
       // P enters the PV product as two bf16 terms, hi = RNE(P) and lo =
       // RNE(P - hi), whose sum is P to 2^-17 relative; a single bf16 P would
       // move an output by up to 2^-9 of the spread of V.
+      uint32_t hw[8], lw[8];
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const float p0 = fast_exp2(fmaf(x[i], kLog2e, -mb));
+        const float p1 = fast_exp2(fmaf(x[i + 1], kLog2e, -mb));
+        split_bf16x2(p0, p1, hw[i >> 1], lw[i >> 1]);
+        l_run += p0;
+        l_run += p1;
+      }
       bf16x8 ph[2], pl[2];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pf = fast_exp2(fmaf(x[i], kLog2e, -mb));
-        const bf16 h = from_f32<bf16>(pf);
-        ph[i >> 3][i & 7] = h;
-        pl[i >> 3][i & 7] = from_f32<bf16>(pf - (float)h);
-        l_run += pf;
+      for (int ks = 0; ks < 2; ++ks) {
+        ph[ks] = __builtin_bit_cast(bf16x8, u32x4{hw[4 * ks], hw[4 * ks + 1], hw[4 * ks + 2],
+                                                  hw[4 * ks + 3]});
+        pl[ks] = __builtin_bit_cast(bf16x8, u32x4{lw[4 * ks], lw[4 * ks + 1], lw[4 * ks + 2],
+                                                  lw[4 * ks + 3]});
       }
       // V^T operand for 16 keys ks*16 + slots (u, e): keys 16ks + 4u + e
       // (e < 4) and 16ks + 8 + 4u + e - 4 (e >= 4), matching ph/pl[ks].  The
