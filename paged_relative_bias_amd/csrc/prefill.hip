@@ -200,9 +200,8 @@ prefill_kernel(const PrefillParams P) {
   const uint64_t vn = reinterpret_cast<uint64_t>(P.v_new);
   // Bias rows of tokens [t0, tend), all heads: row (t, h') at
   // ((t - t0) * Hq + h') * R.
-  const __amdgpu_buffer_rsrc_t rel_rsrc =
-      make_rsrc(static_cast<const T*>(P.rel) + (int64_t)(q0 + t0) * hq * R,
-                (uint32_t)(tend - t0) * (uint32_t)hq * (uint32_t)R * SZ);
+  const T* rel_base = static_cast<const T*>(P.rel) + (int64_t)(q0 + t0) * hq * R;
+  const uint32_t rel_bytes = (uint32_t)(tend - t0) * (uint32_t)hq * (uint32_t)R * SZ;
   const int sbc = SB / VEC;  // bias chunks per row
 
   // ---- loads of one tile into registers ---------------------------------
@@ -221,7 +220,10 @@ prefill_kernel(const PrefillParams P) {
                  head_bytes + (uint32_t)(lane % CPR) * 16u;
   // Bias load i: row r = c / sbc (token rt, head rh), chunk c % sbc.
   uint32_t b_row[C::BIAS_PER];   // row offset | 0x80000000 if the row is unused
-  int b_pos[C::BIAS_PER];        // position of the row's token + (part * VEC << 20)
+  // First entry of the row's window at kt = 0: floor_to(p - (N - 1), VEC);
+  // tiles start at multiples of 16, so the window of tile kt starts kt
+  // entries lower (before the clamp to [0, R - SB]).
+  int b_fb[C::BIAS_PER];
 #pragma unroll
   for (int i = 0; i < C::BIAS_PER; ++i) {
     const int c = i * 64 + lane;
@@ -231,7 +233,7 @@ prefill_kernel(const PrefillParams P) {
     const bool ok = r < 32 && rh < G && rt < tend;
     b_row[i] = ((uint32_t)((rt - t0) * hq + g * G + rh) * (uint32_t)R + (uint32_t)(part * VEC)) * SZ |
                (ok ? 0u : kOOB);
-    b_pos[i] = pbase + rt;
+    b_fb[i] = floor_to(pbase + rt - (N - 1), VEC);
   }
   // Loads of tile kt.  The K/V descriptors of the wave's page end at key
   // je (keys past it, and whole tiles past the last, read zero without
@@ -240,9 +242,11 @@ prefill_kernel(const PrefillParams P) {
   auto issue = [&](Regs& rg, int kt) {
     {
       const int key0 = kt + C::KW * wave;                 // wave-uniform
-      const int pgi = iclamp((key0 >> 4) - pg_lo, 0, P.pid_cap - 1);
+      const int pgi = imin((key0 >> 4) - pg_lo, P.pid_cap - 1);   // >= 0
       const uint64_t page = (uint32_t)__builtin_amdgcn_readfirstlane(pid_lds[pgi]);
-      const uint32_t nrec = sgpr_u32((uint32_t)iclamp(je - (key0 & ~15), 0, 16) * slot_bytes);
+      // Keys of the page up to je (0 past the last tile), as a scalar.
+      const int nk = __builtin_amdgcn_readfirstlane(je - (key0 & ~15));
+      const uint32_t nrec = sgpr_u32((uint32_t)(nk <= 0 ? 0 : (nk >= 16 ? 16 : nk)) * slot_bytes);
       // With an append, slot s of this page is new token (key0 & ~15) + s -
       // pbase: the new rows are addressed like a page whose base sits
       // (key0 & ~15) - pbase rows from k_new's token q0 (only slots of new
@@ -263,14 +267,15 @@ prefill_kernel(const PrefillParams P) {
       }
 
     }
+    // Tiles the wave does not compute read no bias (an empty descriptor).
     const bool wtile = wact && kt < wje && kt + N > wjb;  // wave-uniform
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(rel_base, sgpr_u32(wtile ? rel_bytes : 0u));
 #pragma unroll
     for (int i = 0; i < C::BIAS_PER; ++i) {
       // Distances [p - kt - N + 1, p - kt] clamped to R - 1 lie in the
       // aligned window [base, base + SB).
-      const int base = iclamp(floor_to(b_pos[i] - kt - (N - 1), VEC), 0, R - SB);
-      const uint32_t off = b_row[i] + (uint32_t)base * SZ;
-      rg.b[i] = bload128(rel_rsrc, wtile ? off : kOOB);
+      const int base = iclamp(b_fb[i] - kt, 0, R - SB);
+      rg.b[i] = bload128(rr, b_row[i] + (uint32_t)base * SZ);
     }
   };
   // Tile kt's loads into LDS stage st.
@@ -334,6 +339,10 @@ prefill_kernel(const PrefillParams P) {
   // Later logits may exceed it; P = exp(x - m_ref) stays finite while they
   // exceed it by less than kOver, which a running check confirms; if not,
   // the workgroup streams its keys again with m_ref = the true column max.
+  // Lane constants of compute(): the column's bias window start at kt = 0
+  // (tiles start at multiples of 16) and its lane's distance base.
+  const int fpc = floor_to(pc - (N - 1), VEC);
+  const int pcu = pc - 4 * u;
   float m_ref = kNegInf;
   float l_run = 0.f;
   float m_all = kNegInf;        // running max of this lane's logits
@@ -347,8 +356,8 @@ prefill_kernel(const PrefillParams P) {
     const T* Vs = Ks + N * KP;
     const T* brow = reinterpret_cast<const T*>(bias_lds + (size_t)(wave * 2 + st) * 32 * sbp +
                                                col * sbp);
-    const int base_c = iclamp(floor_to(pc - kt - (N - 1), VEC), 0, R - SB);
-    const int D0 = pc - kt - 4 * u;
+    const int base_c = iclamp(fpc - kt, 0, R - SB);
+    const int D0 = pcu - kt;
     // Bias runs of the fast path, read before the QK product so that their
     // LDS latency overlaps it (in-bounds for every lane; unused on the
     // general path).
