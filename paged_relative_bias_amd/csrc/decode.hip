@@ -8,8 +8,11 @@
 // splits, with a helper that picks the count).
 //
 // Work decomposition.  One workgroup per (group of NH adjacent KV heads,
-// split, sequence b) with one wave per KV head g (NH = 4, 2 or 1: the
-// largest that divides Hkv and fits in LDS; 1 for fp32).  The G query heads
+// split, sequence b) with one wave per KV head g (NH = 2 when Hkv is even
+// and the dtype is bf16, else 1).  Two-wave workgroups of ~79 KB of LDS put
+// two workgroups on a compute unit, each with its own barriers; this
+// measured faster than one four-wave workgroup per compute unit (which
+// shares one barrier among the four waves) and than single-wave ones.  The G query heads
 // of a KV head are its wave's MFMA columns (G <= 16).  A split is a run of
 // at most `chunk_tiles` 32-key tiles of the sequence's visible keys, so
 // every workgroup of a launch streams about the same number of bytes
@@ -586,7 +589,6 @@ template <typename T, int D>
 size_t decode_lds_t(const DecodeParams& p) {
   size_t fixed = Decode<T, D, 1>::fixed_lds();
   if constexpr (sizeof(T) == 2) {
-    if (p.heads_per_wg == 4) fixed = Decode<T, D, 4>::fixed_lds();
     if (p.heads_per_wg == 2) fixed = Decode<T, D, 2>::fixed_lds();
   }
   return fixed + (size_t)p.pid_cap * 4;
@@ -616,7 +618,6 @@ hipError_t launch_decode_h(const DecodeParams& p, hipStream_t stream) {
 template <typename T, int D>
 hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
   if constexpr (sizeof(T) == 2) {
-    if (p.heads_per_wg == 4) return launch_decode_h<T, D, 4>(p, stream);
     if (p.heads_per_wg == 2) return launch_decode_h<T, D, 2>(p, stream);
   }
   if (p.heads_per_wg != 1) return hipErrorInvalidValue;

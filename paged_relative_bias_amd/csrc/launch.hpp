@@ -17,7 +17,7 @@ constexpr int kDecodeKeys = 32;
 // A decode workgroup holds up to kDecodeMaxHeadsPerWG KV heads, one wave
 // each, which load their tiles together.
 constexpr int kDecodeWavesPerCU = 4;
-constexpr int kDecodeMaxHeadsPerWG = 4;
+constexpr int kDecodeMaxHeadsPerWG = 2;
 constexpr int kMaxSplits = 128;
 constexpr int kMaxGroup = 16;
 
@@ -59,7 +59,7 @@ struct DecodeParams {
   int32_t num_blocks, max_blocks, rel_len, window, num_splits;
   int32_t chunk_tiles;  // 32-key tiles per split
   int32_t pid_cap;      // entries of the per-workgroup page-id table (>= 2 * chunk_tiles + 16)
-  int32_t heads_per_wg; // KV heads (one wave each) per workgroup: 4, 2 or 1 (bf16 only above 1)
+  int32_t heads_per_wg; // KV heads (one wave each) per workgroup: 2 or 1 (bf16 only above 1)
   int32_t max_seq_len;  // host bound on seq_lens
   int32_t clamp;        // 1: a visible distance may exceed rel_len - 1
   float scale;
