@@ -90,6 +90,12 @@ __device__ __forceinline__ uint4 bload128(__amdgpu_buffer_rsrc_t r, uint32_t off
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+// The same load with the non-temporal cache policy (aux bit 1 on gfx950):
+// for data read exactly once, such as a decode step's K/V rows and bias.
+__device__ __forceinline__ uint4 bload128_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 __device__ __forceinline__ uint32_t bload32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
 }
