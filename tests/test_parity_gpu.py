@@ -180,8 +180,7 @@ DECODE_CASES = [
     ("mha_g1", 35, [700], 4, 4, 128, 0, 1024, [1, 5]),
     ("g16", 36, [450, 33], 32, 2, 128, 0, 512, [1, 6]),
     ("fp32", 37, [300, 77], 8, 4, 64, 100, 100, [1, 4]),
-    # KV heads per decode workgroup: 1 (Hkv odd), 2 (Hkv = 6), and 2 again
-    # when four heads' LDS stages leave no room for a long page-id table.
+    # KV heads per decode workgroup: 1 (Hkv odd) and 2 (Hkv = 6).
     ("hkv3_one_head_per_wg", 38, [500, 40], 6, 3, 128, 0, 1024, [1, 3]),
     ("hkv6_two_heads_per_wg", 39, [260, 700], 48, 6, 128, 512, 512, [1, 2]),
     ("long_context_table", 44, [20000, 100], 16, 8, 128, 0, 8192, [1, 0]),
