@@ -18,17 +18,21 @@
 //
 // Key tiles of 32 keys sweep the union of the block's visible ranges,
 // double-buffered in LDS:
-//   * K rows (row-major, 16-byte pad) and V rows (row-major, 32-byte pad)
-//     are gathered through the block table: each wave loads 8 keys of the
-//     tile (one page) through a buffer descriptor that ends at the block's
-//     last key (later keys, and tiles past the last, read zero without
-//     traffic); the page ids of the block's range sit in an LDS table;
+//   * K rows and V rows are gathered through the block table: each wave
+//     loads 8 keys of the tile (one page) through a buffer descriptor that
+//     ends at the block's last key (later keys, and tiles past the last,
+//     read zero without traffic); the page ids of the block's range sit in
+//     an LDS table.  bf16 with head_dim 128 (no append) loads them straight
+//     into LDS (rows of D elements, 16-byte chunks XOR-swizzled by row & 7);
+//     the other forms go through registers into rows with a 16-byte (K) or
+//     32-byte (V) pad;
 //   * every wave copies the bias runs of its 32 rows for the tile: for
 //     (token, head) the tile needs one contiguous run of the distance axis,
 //     taken from an aligned window of sb entries with 16-byte loads;
-//   * the next tile's loads are issued into registers before the current
-//     tile is computed and written to the other LDS stage afterwards; the
-//     barriers order LDS only, so the loads stay in flight across them.
+//   * the next tile's loads are issued (into the other LDS stage, or into
+//     registers written to it after the current tile is computed) before
+//     the current tile is computed; the barriers order LDS only, so the
+//     loads stay in flight across them.
 // Per wave and tile:
 //   S^T[key][col] = K . Q^T       32x32x16 bf16 MFMA (32x32x2 f32 for fp32)
 //   x = scale * S + bias          mask by select only on boundary tiles
@@ -105,6 +109,11 @@ prefill_kernel(const PrefillParams P) {
   constexpr int N = C::N, VEC = C::VEC, CPR = C::CPR, KP = C::KP, VP = C::VP, KPI = C::KPI;
   constexpr uint32_t SZ = sizeof(T);
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  // bf16, head_dim 128, no append: K and V rows go from HBM straight into
+  // LDS (16-byte buffer loads with the LDS destination), in rows of D
+  // elements whose 16-byte chunks are XOR-swizzled by (row & 7) so that
+  // the MFMA operand reads spread over the banks.
+  constexpr bool DMA = C::kBF16 && D == 128 && !APPEND;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -215,9 +224,11 @@ prefill_kernel(const PrefillParams P) {
   // lane / CPR, 16-byte chunk lane % CPR.
   uint32_t kv_lane[C::LPT];
 #pragma unroll
-  for (int i = 0; i < C::LPT; ++i)
-    kv_lane[i] = (uint32_t)((C::KW * wave + KPI * i + lane / CPR) & 15) * slot_bytes +
-                 head_bytes + (uint32_t)(lane % CPR) * 16u;
+  for (int i = 0; i < C::LPT; ++i) {
+    const int row = C::KW * wave + KPI * i + lane / CPR;
+    const int ch = DMA ? ((lane % CPR) ^ (row & 7)) : (lane % CPR);
+    kv_lane[i] = (uint32_t)(row & 15) * slot_bytes + head_bytes + (uint32_t)ch * 16u;
+  }
   // Bias load i: row r = c / sbc (token rt, head rh), chunk c % sbc.
   uint32_t b_row[C::BIAS_PER];   // row offset | 0x80000000 if the row is unused
   // First entry of the row's window at kt = 0: floor_to(p - (N - 1), VEC);
@@ -239,7 +250,7 @@ prefill_kernel(const PrefillParams P) {
   // je (keys past it, and whole tiles past the last, read zero without
   // traffic); keys before jb are real cache rows.  Rows the wave does not
   // stage read as kOOB.  No control flow around any load.
-  auto issue = [&](Regs& rg, int kt) {
+  auto issue = [&](Regs& rg, int kt, int st_to) {
     {
       const int key0 = kt + C::KW * wave;                 // wave-uniform
       const int pgi = imin((key0 >> 4) - pg_lo, P.pid_cap - 1);   // >= 0
@@ -260,10 +271,34 @@ prefill_kernel(const PrefillParams P) {
           sgpr_u64(all_new ? vn + new_off : reinterpret_cast<uint64_t>(vg) + page * page_bytes);
       const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const void*>(kb), nrec);
       const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const void*>(vb), nrec);
+      if constexpr (DMA) {
+        // Rows KW * wave + KPI * i .. + KPI - 1 of the stage: one 1 KB block
+        // per load (lane l writes bytes 16 l .. 16 l + 15 after M0).  Lanes
+        // out of the descriptor's range write zeros.  The compiler does not
+        // see these loads: the bias loads issued after them in issue() are
+        // waited for before commit(), which (loads completing in order)
+        // also completes these, and nothing else in the kernel uses M0.
+        const uint32_t kl = sgpr_u32((uint32_t)(st_to * C::stage_bytes()) +
+                                     (uint32_t)(C::KW * wave * D) * SZ);
+        const uint32_t vl = kl + (uint32_t)(N * KP) * SZ;
 #pragma unroll
-      for (int i = 0; i < C::LPT; ++i) {
-        rg.kv[i] = bload128(rk, kv_lane[i]);
-        rg.kv[C::LPT + i] = bload128(rv, kv_lane[i]);
+        for (int i = 0; i < C::LPT; ++i) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+          asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                       :: "s"(kl + (uint32_t)(i * KPI * D) * SZ), "v"(kv_lane[i]), "s"(rk)
+                       : "memory", "m0");
+          asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                       :: "s"(vl + (uint32_t)(i * KPI * D) * SZ), "v"(kv_lane[i]), "s"(rv)
+                       : "memory", "m0");
+#pragma clang diagnostic pop
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < C::LPT; ++i) {
+          rg.kv[i] = bload128(rk, kv_lane[i]);
+          rg.kv[C::LPT + i] = bload128(rv, kv_lane[i]);
+        }
       }
 
     }
@@ -282,12 +317,14 @@ prefill_kernel(const PrefillParams P) {
   auto commit = [&](const Regs& rg, int st, int kt) {
     T* Ks = stage(st);
     T* Vs = Ks + N * KP;
+    if constexpr (!DMA) {
 #pragma unroll
-    for (int i = 0; i < C::LPT; ++i) {
-      const int key = C::KW * wave + KPI * i + lane / CPR;
-      const int chunk = (lane % CPR) * VEC;
-      *reinterpret_cast<uint4*>(Ks + key * KP + chunk) = rg.kv[i];
-      *reinterpret_cast<uint4*>(Vs + key * VP + chunk) = rg.kv[C::LPT + i];
+      for (int i = 0; i < C::LPT; ++i) {
+        const int key = C::KW * wave + KPI * i + lane / CPR;
+        const int chunk = (lane % CPR) * VEC;
+        *reinterpret_cast<uint4*>(Ks + key * KP + chunk) = rg.kv[i];
+        *reinterpret_cast<uint4*>(Vs + key * VP + chunk) = rg.kv[C::LPT + i];
+      }
     }
     if constexpr (APPEND) {
       const int key0 = kt + C::KW * wave;                 // wave-uniform
@@ -369,10 +406,21 @@ prefill_kernel(const PrefillParams P) {
     }
     f32x16 s = f32x16{};
     if constexpr (C::kBF16) {
-      const bf16* krow = Ks + col * KP + 8 * u;
+      if constexpr (DMA) {
+        // Logical chunk 2 st2 + u of row col sits at chunk (2 st2 + u) ^
+        // (col & 7) = 2 ((st2 & 3) ^ y) + z + 8 (st2 >> 2).
+        const int y = (col & 7) >> 1, z = u ^ (col & 1);
+        const bf16* krow = Ks + col * D + 8 * z;
 #pragma unroll
-      for (int st2 = 0; st2 < C::QSTEPS; ++st2)
-        s = mfma32(*reinterpret_cast<const bf16x8*>(krow + 16 * st2), qop[st2], s);
+        for (int st2 = 0; st2 < C::QSTEPS; ++st2)
+          s = mfma32(*reinterpret_cast<const bf16x8*>(krow + 16 * ((st2 & 3) ^ y) + 64 * (st2 >> 2)),
+                     qop[st2], s);
+      } else {
+        const bf16* krow = Ks + col * KP + 8 * u;
+#pragma unroll
+        for (int st2 = 0; st2 < C::QSTEPS; ++st2)
+          s = mfma32(*reinterpret_cast<const bf16x8*>(krow + 16 * st2), qop[st2], s);
+      }
     } else {
       const float* krow = Ks + col * KP + u;
 #pragma unroll
@@ -470,15 +518,24 @@ prefill_kernel(const PrefillParams P) {
       // at key (4u + j/4), columns d0 + 4*(j%4) .. +3.
       const int jj = lane & 15;
       const int dgrp = (lane >> 4) & 1;
+      // DMA layout: element e of row r sits at chunk (e / 8) ^ (r & 7); the
+      // rows 4 u + jj / 4 (+ 8, + 16) share r & 7, so two bases (even and
+      // odd dt) plus immediate offsets cover every read.
+      const int vr = 4 * u + (jj >> 2), vx = vr & 7;
+      const int vq = 8 * ((2 * dgrp + ((jj & 3) >> 1)) ^ (vx & 3)) + 4 * (jj & 1);
+      const T* vbe = Vs + vr * D + vq + 32 * (vx >> 2);
+      const T* vbo = Vs + vr * D + vq - 32 * (vx >> 2);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const T* vb = Vs + (4 * u + (jj >> 2)) * VP + 32 * dt + 16 * dgrp + 4 * (jj & 3);
+        const T* vb = DMA ? (dt & 1 ? vbo : vbe) + 32 * dt
+                          : Vs + (4 * u + (jj >> 2)) * VP + 32 * dt + 16 * dgrp + 4 * (jj & 3);
+        constexpr int VPd = DMA ? D : VP;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(vb + (16 * ks) * VP));
+              (__attribute__((address_space(3))) i16x4*)(vb + (16 * ks) * VPd));
           const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(vb + (16 * ks + 8) * VP));
+              (__attribute__((address_space(3))) i16x4*)(vb + (16 * ks + 8) * VPd));
           const i16x8 a16 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           acc[dt] = mfma32(__builtin_bit_cast(bf16x8, a16), ph[ks], acc[dt]);
           acc[dt] = mfma32(__builtin_bit_cast(bf16x8, a16), pl[ks], acc[dt]);
@@ -528,17 +585,17 @@ prefill_kernel(const PrefillParams P) {
   while (true) {
     lds_barrier();                                       // page ids ready
     int kt = jb & ~15;
-    issue(ra, kt);
+    issue(ra, kt, 0);
     commit(ra, 0, kt);
     lds_barrier();
     while (true) {
-      issue(ra, kt + N);
+      issue(ra, kt + N, 1);
       compute(kt, 0);
       if (kt + N >= je) break;                           // workgroup-uniform
       commit(ra, 1, kt + N);
       lds_barrier();
       kt += N;
-      issue(ra, kt + N);
+      issue(ra, kt + N, 0);
       compute(kt, 1);
       if (kt + N >= je) break;
       commit(ra, 0, kt + N);
