@@ -110,9 +110,13 @@ prefill_kernel(const PrefillParams P) {
   constexpr uint32_t SZ = sizeof(T);
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   // bf16, head_dim 128, no append: K and V rows go from HBM straight into
-  // LDS (16-byte buffer loads with the LDS destination), in rows of D
-  // elements whose 16-byte chunks are XOR-swizzled by (row & 7) so that
-  // the MFMA operand reads spread over the banks.
+  // LDS (16-byte buffer loads with the LDS destination) in rows of D
+  // elements, laid out so that the MFMA operand reads hit distinct banks:
+  //   K row r at byte r * 256 + 128 * (r >> 3), chunk c at c ^ (r & 7)
+  //     (16 lanes reading rows r .. r + 15 at one logical chunk cover all
+  //     64 banks; groups of 8 rows are 128 bytes apart, 8576 bytes in all);
+  //   V row r at byte r * 256, chunk c at c ^ (4 * (r & 3)) (a transposed
+  //     read's four rows then use 16 different chunks).
   constexpr bool DMA = C::kBF16 && D == 128 && !APPEND;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -223,11 +227,16 @@ prefill_kernel(const PrefillParams P) {
   // multiples of 16); its load i of K (and of V) covers keys KW*w + KPI*i +
   // lane / CPR, 16-byte chunk lane % CPR.
   uint32_t kv_lane[C::LPT];
+  uint32_t v_lane[C::LPT];       // V offsets (the DMA layout swizzles V differently)
 #pragma unroll
   for (int i = 0; i < C::LPT; ++i) {
     const int row = C::KW * wave + KPI * i + lane / CPR;
-    const int ch = DMA ? ((lane % CPR) ^ (row & 7)) : (lane % CPR);
-    kv_lane[i] = (uint32_t)(row & 15) * slot_bytes + head_bytes + (uint32_t)ch * 16u;
+    // Lane l writes physical chunk l % CPR of its row, so it fetches the
+    // logical chunk that the layout puts there.
+    const int chk = DMA ? ((lane % CPR) ^ (row & 7)) : (lane % CPR);
+    const int chv = DMA ? ((lane % CPR) ^ (4 * (row & 3))) : (lane % CPR);
+    kv_lane[i] = (uint32_t)(row & 15) * slot_bytes + head_bytes + (uint32_t)chk * 16u;
+    v_lane[i] = (uint32_t)(row & 15) * slot_bytes + head_bytes + (uint32_t)chv * 16u;
   }
   // Bias load i: row r = c / sbc (token rt, head rh), chunk c % sbc.
   uint32_t b_row[C::BIAS_PER];   // row offset | 0x80000000 if the row is unused
@@ -278,19 +287,21 @@ prefill_kernel(const PrefillParams P) {
         // see these loads: the bias loads issued after them in issue() are
         // waited for before commit(), which (loads completing in order)
         // also completes these, and nothing else in the kernel uses M0.
-        const uint32_t kl = sgpr_u32((uint32_t)(st_to * C::stage_bytes()) +
-                                     (uint32_t)(C::KW * wave * D) * SZ);
-        const uint32_t vl = kl + (uint32_t)(N * KP) * SZ;
+        // Rows of load i: 4-row block kb = KW * wave / KPI + i, K at byte
+        // kb * 1024 + 128 * (kb >> 1), V at kb * 1024.
+        const uint32_t sl = sgpr_u32((uint32_t)(st_to * C::stage_bytes()));
+        const int kb0 = C::KW * wave / KPI;                // wave-uniform
 #pragma unroll
         for (int i = 0; i < C::LPT; ++i) {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+          const int kb = kb0 + i;
+          const uint32_t klds = sgpr_u32(sl + (uint32_t)kb * 1024u + 128u * (uint32_t)(kb >> 1));
+          const uint32_t vlds = sgpr_u32(sl + (uint32_t)(N * KP) * SZ + (uint32_t)kb * 1024u);
           asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                       :: "s"(kl + (uint32_t)(i * KPI * D) * SZ), "v"(kv_lane[i]), "s"(rk)
-                       : "memory", "m0");
+                       :: "s"(klds), "v"(kv_lane[i]), "s"(rk) : "memory", "m0");
           asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                       :: "s"(vl + (uint32_t)(i * KPI * D) * SZ), "v"(kv_lane[i]), "s"(rv)
-                       : "memory", "m0");
+                       :: "s"(vlds), "v"(v_lane[i]), "s"(rv) : "memory", "m0");
 #pragma clang diagnostic pop
         }
       } else {
@@ -410,7 +421,7 @@ prefill_kernel(const PrefillParams P) {
         // Logical chunk 2 st2 + u of row col sits at chunk (2 st2 + u) ^
         // (col & 7) = 2 ((st2 & 3) ^ y) + z + 8 (st2 >> 2).
         const int y = (col & 7) >> 1, z = u ^ (col & 1);
-        const bf16* krow = Ks + col * D + 8 * z;
+        const bf16* krow = Ks + col * D + 64 * (col >> 3) + 8 * z;
 #pragma unroll
         for (int st2 = 0; st2 < C::QSTEPS; ++st2)
           s = mfma32(*reinterpret_cast<const bf16x8*>(krow + 16 * ((st2 & 3) ^ y) + 64 * (st2 >> 2)),
@@ -518,16 +529,15 @@ prefill_kernel(const PrefillParams P) {
       // at key (4u + j/4), columns d0 + 4*(j%4) .. +3.
       const int jj = lane & 15;
       const int dgrp = (lane >> 4) & 1;
-      // DMA layout: element e of row r sits at chunk (e / 8) ^ (r & 7); the
-      // rows 4 u + jj / 4 (+ 8, + 16) share r & 7, so two bases (even and
-      // odd dt) plus immediate offsets cover every read.
-      const int vr = 4 * u + (jj >> 2), vx = vr & 7;
-      const int vq = 8 * ((2 * dgrp + ((jj & 3) >> 1)) ^ (vx & 3)) + 4 * (jj & 1);
-      const T* vbe = Vs + vr * D + vq + 32 * (vx >> 2);
-      const T* vbo = Vs + vr * D + vq - 32 * (vx >> 2);
+      // DMA layout: element e of row r sits at chunk (e / 8) ^ (4 (r & 3));
+      // the rows 4 u + jj / 4 (+ 8, + 16) share r & 3 = jj / 4, so d-block
+      // dt of the lane's columns starts 32 (dt ^ (jj / 4)) elements into the
+      // row: one base per dt plus immediate row offsets.
+      const T* vbase = Vs + (4 * u + (jj >> 2)) * D + 8 * (2 * dgrp + ((jj & 3) >> 1)) +
+                       4 * (jj & 1);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const T* vb = DMA ? (dt & 1 ? vbo : vbe) + 32 * dt
+        const T* vb = DMA ? vbase + 32 * (dt ^ (jj >> 2))
                           : Vs + (4 * u + (jj >> 2)) * VP + 32 * dt + 16 * dgrp + 4 * (jj & 3);
         constexpr int VPd = DMA ? D : VP;
 #pragma unroll
