@@ -145,6 +145,23 @@ def test_prefill_deterministic_and_page_permutation_bitexact():
     assert torch.equal(o1.view(torch.int16), o3.view(torch.int16))
 
 
+def test_prefill_stale_lds_never_leaks():
+    """Keys past a block's last key reach LDS as zeros (their P is 0, so a
+    stale non-finite V row there would turn the output into NaN).  A prefill
+    over K/V pools that are entirely NaN first leaves NaN in the LDS stages
+    of every compute unit it ran on; a ragged prefill right after, whose
+    tiles end inside pages, must still match the oracle."""
+    b = _mk(7, [700, 333, 97, 45], [700, 333, 97, 45], Hq=48, Hkv=16, W=512, R=512)
+    _say("prefill after a NaN-filled run (stale LDS)")
+    poisoned = U.Dev(b)
+    poisoned.k.fill_(float("nan"))
+    poisoned.v.fill_(float("nan"))
+    U.prefill(poisoned)
+    torch.cuda.synchronize()
+    ref, _ = oracle.run_batch(b)
+    U.compare(U.prefill(U.Dev(b)), ref, "bf16", "after_nan_run")
+
+
 def test_prefill_chunked_equals_whole():
     """Two chunked calls (first k tokens, then the rest on top) give the same
     rows as one call.  Key tiles start at key 0 in both (full causal), and a
