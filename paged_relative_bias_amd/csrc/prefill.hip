@@ -23,9 +23,9 @@
 //     ends at the block's last key (later keys, and tiles past the last,
 //     read zero without traffic); the page ids of the block's range sit in
 //     an LDS table.  bf16 with head_dim 128 (no append) loads them straight
-//     into LDS (rows of D elements, 16-byte chunks XOR-swizzled by row & 7);
-//     the other forms go through registers into rows with a 16-byte (K) or
-//     32-byte (V) pad;
+//     into LDS in a bank-conflict-free layout (rows of D elements with
+//     XOR-swizzled 16-byte chunks, see DMA below); the other forms go
+//     through registers into rows with a 16-byte (K) or 32-byte (V) pad;
 //   * every wave copies the bias runs of its 32 rows for the tile: for
 //     (token, head) the tile needs one contiguous run of the distance axis,
 //     taken from an aligned window of sb entries with 16-byte loads;
