@@ -32,13 +32,15 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 // Two fp32 values p0, p1 as sums of two bf16 terms, packed two per word
 // (p0 in the low half): hi = RNE(p), lo = RNE(p - hi).  p - hi is exact in
 // fp32, so hi + lo equals p to 2^-17 relative.  One packed conversion each
-// for hi and lo, and hi widened back by a shift and a mask.
-__device__ __forceinline__ void split_bf16x2(float p0, float p1, uint32_t& hi, uint32_t& lo) {
-  const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p0, p1}, bf16x2));
-  const float h0 = __builtin_bit_cast(float, h << 16);
-  const float h1 = __builtin_bit_cast(float, h & 0xffff0000u);
-  hi = h;
-  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p0 - h0, p1 - h1}, bf16x2));
+// for hi and lo, and hi widened back by a shift and a mask.  The two halves
+// are separate calls so that a caller can issue work on hi before lo exists.
+__device__ __forceinline__ uint32_t bf16x2_hi(float p0, float p1) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p0, p1}, bf16x2));
+}
+__device__ __forceinline__ uint32_t bf16x2_lo(float p0, float p1, uint32_t hi) {
+  const float h0 = __builtin_bit_cast(float, hi << 16);
+  const float h1 = __builtin_bit_cast(float, hi & 0xffff0000u);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p0 - h0, p1 - h1}, bf16x2));
 }
 
 // 2^x on the transcendental unit.  Callers pass -inf (giving 0) or x below

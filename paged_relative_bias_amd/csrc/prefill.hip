@@ -506,27 +506,26 @@ prefill_kernel(const PrefillParams P) {
       // P enters the PV product as two bf16 terms, hi = RNE(P) and lo =
       // RNE(P - hi), whose sum is P to 2^-17 relative; a single bf16 P would
       // move an output by up to 2^-9 of the spread of V.
-      uint32_t hw[8], lw[8];
+      // Exponentials and the hi terms first; the lo terms and the row sum
+      // are computed while the hi-term MFMAs run.
+      float pv[16];
+      uint32_t hw[8];
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
-        const float p0 = fast_exp2(fmaf(x[i], kLog2e, -mb));
-        const float p1 = fast_exp2(fmaf(x[i + 1], kLog2e, -mb));
-        split_bf16x2(p0, p1, hw[i >> 1], lw[i >> 1]);
-        l_run += p0;
-        l_run += p1;
+        pv[i] = fast_exp2(fmaf(x[i], kLog2e, -mb));
+        pv[i + 1] = fast_exp2(fmaf(x[i + 1], kLog2e, -mb));
+        hw[i >> 1] = bf16x2_hi(pv[i], pv[i + 1]);
       }
-      bf16x8 ph[2], pl[2];
+      bf16x8 ph[2];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      for (int ks = 0; ks < 2; ++ks)
         ph[ks] = __builtin_bit_cast(bf16x8, u32x4{hw[4 * ks], hw[4 * ks + 1], hw[4 * ks + 2],
                                                   hw[4 * ks + 3]});
-        pl[ks] = __builtin_bit_cast(bf16x8, u32x4{lw[4 * ks], lw[4 * ks + 1], lw[4 * ks + 2],
-                                                  lw[4 * ks + 3]});
-      }
       // V^T operand for 16 keys ks*16 + slots (u, e): keys 16ks + 4u + e
       // (e < 4) and 16ks + 8 + 4u + e - 4 (e >= 4), matching ph/pl[ks].  The
       // 16-lane groups of a transposed read cover d0..d0+15: lane j points
-      // at key (4u + j/4), columns d0 + 4*(j%4) .. +3.
+      // at key (4u + j/4), columns d0 + 4*(j%4) .. +3.  All of them are read
+      // before the first PV MFMA, as both P terms use them.
       const int jj = lane & 15;
       const int dgrp = (lane >> 4) & 1;
       // DMA layout: element e of row r sits at chunk (e / 8) ^ (4 (r & 3));
@@ -535,6 +534,7 @@ prefill_kernel(const PrefillParams P) {
       // row: one base per dt plus immediate row offsets.
       const T* vbase = Vs + (4 * u + (jj >> 2)) * D + 8 * (2 * dgrp + ((jj & 3) >> 1)) +
                        4 * (jj & 1);
+      bf16x8 va[D / 32][2];
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
         const T* vb = DMA ? vbase + 32 * (dt ^ (jj >> 2))
@@ -547,10 +547,29 @@ prefill_kernel(const PrefillParams P) {
           const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (__attribute__((address_space(3))) i16x4*)(vb + (16 * ks + 8) * VPd));
           const i16x8 a16 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          acc[dt] = mfma32(__builtin_bit_cast(bf16x8, a16), ph[ks], acc[dt]);
-          acc[dt] = mfma32(__builtin_bit_cast(bf16x8, a16), pl[ks], acc[dt]);
+          va[dt][ks] = __builtin_bit_cast(bf16x8, a16);
         }
       }
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) acc[dt] = mfma32(va[dt][ks], ph[ks], acc[dt]);
+      uint32_t lw[8];
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        lw[i >> 1] = bf16x2_lo(pv[i], pv[i + 1], hw[i >> 1]);
+        l_run += pv[i];
+        l_run += pv[i + 1];
+      }
+      bf16x8 pl[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        pl[ks] = __builtin_bit_cast(bf16x8, u32x4{lw[4 * ks], lw[4 * ks + 1], lw[4 * ks + 2],
+                                                  lw[4 * ks + 3]});
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) acc[dt] = mfma32(va[dt][ks], pl[ks], acc[dt]);
     } else {
       float pf[16];
 #pragma unroll
