@@ -148,7 +148,9 @@ def main():
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=10)
+    # Prefill launches (~0.7 ms) need about 20 ms of back-to-back work before
+    # their duration settles; 50 untimed steps cover that for every workload.
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="local_decode",
                     choices=["local_decode", "global_decode", "local_prefill",
                              "global_mixed", "global_mixed_split", "tiny_prefill",
