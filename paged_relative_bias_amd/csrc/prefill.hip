@@ -437,6 +437,44 @@ prefill_kernel(const PrefillParams P) {
 #pragma unroll
       for (int st2 = 0; st2 < C::QSTEPS; ++st2) s = mfma32(krow[2 * st2], qop[st2], s);
     }
+    // V^T operands of this tile (bf16).  The plain kernel reads them here,
+    // so that their LDS latency runs under the softmax arithmetic; the
+    // append instance reads them just before the PV product (reading them
+    // here makes it spill).
+    bf16x8 va[D / 32][2];
+    auto read_vt = [&]() {
+      if constexpr (C::kBF16) {
+        // V^T operand for 16 keys ks*16 + slots (u, e): keys 16ks + 4u + e
+        // (e < 4) and 16ks + 8 + 4u + e - 4 (e >= 4), matching ph/pl[ks].  The
+        // 16-lane groups of a transposed read cover d0..d0+15: lane j points
+        // at key (4u + j/4), columns d0 + 4*(j%4) .. +3.  All of them are read
+        // before the first PV MFMA, as both P terms use them.
+        const int jj = lane & 15;
+        const int dgrp = (lane >> 4) & 1;
+        // DMA layout: element e of row r sits at chunk (e / 8) ^ (4 (r & 3));
+        // the rows 4 u + jj / 4 (+ 8, + 16) share r & 3 = jj / 4, so d-block
+        // dt of the lane's columns starts 32 (dt ^ (jj / 4)) elements into the
+        // row: one base per dt plus immediate row offsets.
+        const T* vbase = Vs + (4 * u + (jj >> 2)) * D + 8 * (2 * dgrp + ((jj & 3) >> 1)) +
+                         4 * (jj & 1);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          const T* vb = DMA ? vbase + 32 * (dt ^ (jj >> 2))
+                            : Vs + (4 * u + (jj >> 2)) * VP + 32 * dt + 16 * dgrp + 4 * (jj & 3);
+          constexpr int VPd = DMA ? D : VP;
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4*)(vb + (16 * ks) * VPd));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4*)(vb + (16 * ks + 8) * VPd));
+            const i16x8 a16 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            va[dt][ks] = __builtin_bit_cast(bf16x8, a16);
+          }
+        }
+      }
+    };
+    if constexpr (C::kBF16 && !APPEND) read_vt();
     // x = scale * S + bias (natural-log units); lane holds keys
     // kt + 8*(i/4) + 4*u + i%4, i.e. distances d_i = pc - kt - 4u - c_i with
     // c_i = 8*(i/4) + i%4.
@@ -521,35 +559,7 @@ prefill_kernel(const PrefillParams P) {
       for (int ks = 0; ks < 2; ++ks)
         ph[ks] = __builtin_bit_cast(bf16x8, u32x4{hw[4 * ks], hw[4 * ks + 1], hw[4 * ks + 2],
                                                   hw[4 * ks + 3]});
-      // V^T operand for 16 keys ks*16 + slots (u, e): keys 16ks + 4u + e
-      // (e < 4) and 16ks + 8 + 4u + e - 4 (e >= 4), matching ph/pl[ks].  The
-      // 16-lane groups of a transposed read cover d0..d0+15: lane j points
-      // at key (4u + j/4), columns d0 + 4*(j%4) .. +3.  All of them are read
-      // before the first PV MFMA, as both P terms use them.
-      const int jj = lane & 15;
-      const int dgrp = (lane >> 4) & 1;
-      // DMA layout: element e of row r sits at chunk (e / 8) ^ (4 (r & 3));
-      // the rows 4 u + jj / 4 (+ 8, + 16) share r & 3 = jj / 4, so d-block
-      // dt of the lane's columns starts 32 (dt ^ (jj / 4)) elements into the
-      // row: one base per dt plus immediate row offsets.
-      const T* vbase = Vs + (4 * u + (jj >> 2)) * D + 8 * (2 * dgrp + ((jj & 3) >> 1)) +
-                       4 * (jj & 1);
-      bf16x8 va[D / 32][2];
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        const T* vb = DMA ? vbase + 32 * (dt ^ (jj >> 2))
-                          : Vs + (4 * u + (jj >> 2)) * VP + 32 * dt + 16 * dgrp + 4 * (jj & 3);
-        constexpr int VPd = DMA ? D : VP;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(vb + (16 * ks) * VPd));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(vb + (16 * ks + 8) * VPd));
-          const i16x8 a16 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          va[dt][ks] = __builtin_bit_cast(bf16x8, a16);
-        }
-      }
+      if constexpr (APPEND) read_vt();
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
