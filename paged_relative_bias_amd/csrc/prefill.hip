@@ -415,32 +415,10 @@ prefill_kernel(const PrefillParams P) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) __builtin_memcpy(&brun[k], bb + 24 - 8 * k, 8);
     }
-    f32x16 s = f32x16{};
-    if constexpr (C::kBF16) {
-      if constexpr (DMA) {
-        // Logical chunk 2 st2 + u of row col sits at chunk (2 st2 + u) ^
-        // (col & 7) = 2 ((st2 & 3) ^ y) + z + 8 (st2 >> 2).
-        const int y = (col & 7) >> 1, z = u ^ (col & 1);
-        const bf16* krow = Ks + col * D + 64 * (col >> 3) + 8 * z;
-#pragma unroll
-        for (int st2 = 0; st2 < C::QSTEPS; ++st2)
-          s = mfma32(*reinterpret_cast<const bf16x8*>(krow + 16 * ((st2 & 3) ^ y) + 64 * (st2 >> 2)),
-                     qop[st2], s);
-      } else {
-        const bf16* krow = Ks + col * KP + 8 * u;
-#pragma unroll
-        for (int st2 = 0; st2 < C::QSTEPS; ++st2)
-          s = mfma32(*reinterpret_cast<const bf16x8*>(krow + 16 * st2), qop[st2], s);
-      }
-    } else {
-      const float* krow = Ks + col * KP + u;
-#pragma unroll
-      for (int st2 = 0; st2 < C::QSTEPS; ++st2) s = mfma32(krow[2 * st2], qop[st2], s);
-    }
     // V^T operands of this tile (bf16).  The plain kernel reads them here,
-    // so that their LDS latency runs under the softmax arithmetic; the
-    // append instance reads them just before the PV product (reading them
-    // here makes it spill).
+    // so that their LDS latency runs under the QK product and the softmax
+    // arithmetic; the append instance reads them just before the PV product
+    // (reading them early makes it spill).
     bf16x8 va[D / 32][2];
     auto read_vt = [&]() {
       if constexpr (C::kBF16) {
@@ -475,6 +453,28 @@ prefill_kernel(const PrefillParams P) {
       }
     };
     if constexpr (C::kBF16 && !APPEND) read_vt();
+    f32x16 s = f32x16{};
+    if constexpr (C::kBF16) {
+      if constexpr (DMA) {
+        // Logical chunk 2 st2 + u of row col sits at chunk (2 st2 + u) ^
+        // (col & 7) = 2 ((st2 & 3) ^ y) + z + 8 (st2 >> 2).
+        const int y = (col & 7) >> 1, z = u ^ (col & 1);
+        const bf16* krow = Ks + col * D + 64 * (col >> 3) + 8 * z;
+#pragma unroll
+        for (int st2 = 0; st2 < C::QSTEPS; ++st2)
+          s = mfma32(*reinterpret_cast<const bf16x8*>(krow + 16 * ((st2 & 3) ^ y) + 64 * (st2 >> 2)),
+                     qop[st2], s);
+      } else {
+        const bf16* krow = Ks + col * KP + 8 * u;
+#pragma unroll
+        for (int st2 = 0; st2 < C::QSTEPS; ++st2)
+          s = mfma32(*reinterpret_cast<const bf16x8*>(krow + 16 * st2), qop[st2], s);
+      }
+    } else {
+      const float* krow = Ks + col * KP + u;
+#pragma unroll
+      for (int st2 = 0; st2 < C::QSTEPS; ++st2) s = mfma32(krow[2 * st2], qop[st2], s);
+    }
     // x = scale * S + bias (natural-log units); lane holds keys
     // kt + 8*(i/4) + 4*u + i%4, i.e. distances d_i = pc - kt - 4u - c_i with
     // c_i = 8*(i/4) + i%4.
