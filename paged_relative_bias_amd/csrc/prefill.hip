@@ -47,6 +47,10 @@
 //                                 from registers as two bf16 terms (hi =
 //                                 RNE(P), lo = RNE(P - hi)), two MFMAs;
 //                                 row sums of P in fp32.
+// Issue order within a tile (bf16): bias runs and V^T operands are read
+// from LDS first, so that their latency runs under the QK MFMAs and the
+// softmax; the hi-term PV MFMAs go out before the lo terms and the row sum
+// are computed, which then run under them.
 #include <type_traits>
 
 #include "device.hpp"
