@@ -5,13 +5,23 @@ One step is one call of the library's hot path on one synthetic batch, with
 its inputs already resident in HBM:
   * decode workloads: inkling_rel_attn_decode (split-KV decode kernel, plus
     the log-sum-exp merge kernel when it uses more than one split);
-  * prefill workloads: inkling_rel_attn_prefill.
-The default workload is the local-layer decode batch (64 sequences, contexts
-U[1024, 8192], 48 query / 16 KV heads, head_dim 128, window 512, bf16).
+  * prefill workloads: inkling_rel_attn_prefill;
+  * global_mixed_split: prefill of the 4 chunks, then decode of the 48 rows,
+    back to back on one stream.
+
+The JSON line's headline (`value`, `roofline`, `cpu_baseline`) is the
+local-layer decode batch (64 sequences, contexts U[1024, 8192], 48 query /
+16 KV heads, head_dim 128, window 512, bf16).  Without --workload the line
+also carries `workloads`: one record of the same fields for every other
+serving configuration (global decode at the library's split count and at 1,
+8 and 32 splits, local prefill, the global mixed batch as one call and
+split, long-context global decode, and the smaller model's shapes).
 
 Timing: W untimed warm-up steps, then exactly K steps bracketed by
-torch.cuda.synchronize(); HIP events on the launch stream around every step
-give the per-launch duration used for the roofline.  Consecutive steps read
+torch.cuda.synchronize(); two HIP events on the launch stream around the
+timed region give the back-to-back mean, and a separate pass with an event
+pair around every step (at least 50) gives the median and p10/p90 launch
+durations.  The roofline fractions use the median.  Consecutive steps read
 different device copies of the inputs (replicas rotated round-robin, at
 least 512 MB apart) so no step finds its data in the 256 MB Infinity Cache
 left behind by the previous one, as in a real forward where consecutive
@@ -22,6 +32,7 @@ Prints ONE JSON line on stdout; diagnostics go to stderr.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import math
@@ -42,6 +53,22 @@ MALL_BYTES = 256 << 20
 DECODE_KERNEL_SRC = os.path.join(ROOT, "paged_relative_bias_amd", "csrc", "decode.hip")
 PREFILL_KERNEL_SRC = os.path.join(ROOT, "paged_relative_bias_amd", "csrc", "prefill.hip")
 PROFILES = os.path.join(ROOT, "profiles")
+HEADLINE = "local_decode"
+# The other records: generator -> [(record name, decode split count (0 =
+# the library's choice))]; each generated batch serves all of its records.
+SECONDARY = [
+    ("global_decode", [("global_decode", 0), ("global_decode_s1", 1),
+                       ("global_decode_s8", 8), ("global_decode_s32", 32)]),
+    ("local_prefill", [("local_prefill", 0)]),
+    ("global_mixed", [("global_mixed", 0), ("global_mixed_split", 0)]),
+    ("long_global_decode", [("long_global_decode", 0)]),
+    ("small_local_decode", [("small_local_decode", 0)]),
+    ("small_global_decode", [("small_global_decode", 0)]),
+    ("small_local_prefill", [("small_local_prefill", 0)]),
+]
+WORKLOAD_CHOICES = ["local_decode", "global_decode", "local_prefill", "global_mixed",
+                    "global_mixed_split", "tiny_prefill", "long_global_decode",
+                    "small_local_decode", "small_global_decode", "small_local_prefill"]
 
 
 def log(*a):
@@ -66,7 +93,7 @@ def algorithmic(batch):
     e = 2 if batch.dtype == "bf16" else 4
     Hq, Hkv, D, W = batch.num_q_heads, batch.num_kv_heads, batch.head_dim, batch.window
     R = batch.rel_len
-    kv = bias = pages = 0
+    kv = pages = 0
     pairs = entries = 0
     for b in range(batch.num_seqs):
         n, L = int(batch.q_lens[b]), int(batch.seq_lens[b])
@@ -92,20 +119,25 @@ def source_hash(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_from_profiles(workload, kernel_src, launches_per_step=1):
-    """HBM bytes per launch from committed rocprofv3 counter summaries, if
-    they were taken on the current kernel source; else None."""
-    path = os.path.join(PROFILES, f"traffic_{workload}.json")
+def traffic_from_profiles(record, kernel_srcs):
+    """HBM bytes per step from committed rocprofv3 counter summaries, if they
+    were taken on the current kernel sources; else None."""
+    path = os.path.join(PROFILES, f"traffic_{record}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha256_16") != source_hash(kernel_src):
+    want = rec.get("kernel_sources_sha256_16") or {}
+    if not want:
         return None
-    return rec.get("hbm_bytes_per_launch")
+    for src in kernel_srcs:
+        rel = os.path.relpath(src, ROOT)
+        if want.get(rel) != source_hash(src):
+            return None
+    return rec.get("hbm_bytes_per_step")
 
 
-def cpu_baseline(batch, budget_s=20.0):
+def cpu_baseline(batch, budget_s):
     """The fp64 oracle as it stands, on the host cores, over the whole batch
     (decode) or over a bounded, seeded subset of (row, head) pairs (prefill),
     scaled to query tokens per second."""
@@ -114,17 +146,16 @@ def cpu_baseline(batch, budget_s=20.0):
     threads = oracle.max_threads()
     Hq = batch.num_q_heads
     total_rows = batch.total_q * Hq
-    if batch.is_decode():
+    rng = np.random.default_rng(0)
+    probe = rng.choice(total_rows, size=min(256, total_rows), replace=False)
+    t0 = time.perf_counter()
+    oracle.run_batch(batch, rows=probe)
+    per_row = (time.perf_counter() - t0) / len(probe)
+    if per_row * total_rows <= budget_s:
         rows = None
-        sample = f"whole batch: {batch.num_seqs} sequences x {Hq} heads"
         frac = 1.0
+        sample = f"whole batch: {batch.total_q} rows x {Hq} heads"
     else:
-        # Size the subset from a quick probe so the run takes ~budget_s.
-        rng = np.random.default_rng(0)
-        probe = rng.choice(total_rows, size=min(256, total_rows), replace=False)
-        t0 = time.perf_counter()
-        oracle.run_batch(batch, rows=probe)
-        per_row = (time.perf_counter() - t0) / len(probe)
         n = int(min(total_rows, max(256, budget_s / max(per_row, 1e-9))))
         rows = rng.choice(total_rows, size=n, replace=False)
         frac = n / total_rows
@@ -138,9 +169,239 @@ def cpu_baseline(batch, budget_s=20.0):
             break
     dt = (time.perf_counter() - t0) / runs
     tokens = batch.total_q * frac
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads,
+    return {"value": round(tokens / dt, 1), "unit": "tokens/s", "cores": threads,
             "kind": "oracle", "sample": sample, "seconds_per_run": round(dt, 4),
             "runs": runs}
+
+
+def spike_bias(batch, amount=60.0):
+    """+amount on the distance-0 bias entry of every row: the query's own key
+    then has a logit far above every other, which sends every workgroup of
+    the fixed-reference softmax into its second pass."""
+    import dataclasses
+    import torch
+    rel = batch.rel_logits.clone()
+    rel[:, :, 0] = (rel[:, :, 0].float() + amount).to(rel.dtype)
+    return dataclasses.replace(batch, rel_logits=rel)
+
+
+class Workload:
+    """Device replicas of one configuration and the pre-marshalled calls of
+    one step on each."""
+
+    def __init__(self, name, batch, *, splits, append, graph, replicas, dev):
+        import torch
+        from paged_relative_bias_amd import binding, inputs
+
+        self.name = name
+        self.batch = batch
+        split_mixed = name == "global_mixed_split"
+        parts = list(inputs.split_mixed(batch)) if split_mixed else [batch]
+        self.parts = [p for p in parts if p.num_seqs > 0]
+        alg = [algorithmic(p) for p in self.parts]
+        self.step_bytes = sum(a["bytes"] for a in alg)
+        if append:
+            # k_new and v_new read once, and the same rows written to the cache.
+            self.step_bytes += 2 * 2 * batch.total_q * batch.num_kv_heads * batch.head_dim * (
+                2 if batch.dtype == "bf16" else 4)
+        self.step_flops = sum(a["flops"] for a in alg)
+        self.tokens = sum(p.total_q for p in self.parts)
+        self.replicas = replicas or max(2, math.ceil(2 * MALL_BYTES / self.step_bytes) + 1)
+        self.stream = torch.cuda.current_stream()
+        self.launch_stream = torch.cuda.Stream() if graph else self.stream
+        self.kernel_srcs = set()
+        self.splits_used = []
+        calls, self.keep = [], []
+        for r in range(self.replicas):
+            rc = []
+            for p in self.parts:
+                q = p.q.to(dev)
+                k, v = p.k_cache.to(dev), p.v_cache.to(dev)
+                rel = p.rel_logits.to(dev)
+                bt = torch.from_numpy(p.block_table).to(dev)
+                sl = torch.from_numpy(p.seq_lens).to(dev)
+                out = torch.empty_like(q)
+                if p.is_decode() and name != "global_mixed":
+                    d = binding.dims_for(q, k, bt, rel, num_seqs=p.num_seqs, max_q_len=1,
+                                         max_seq_len=p.max_seq_len)
+                    s = splits or binding.num_splits(d, p.window, 0)
+                    need = binding.decode_workspace_bytes(d, p.window, s)
+                    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev) if need else None
+                    a, dims = binding.decode_args(q, k, v, bt, sl, rel, p.window, p.scale, out,
+                                                  max_seq_len=p.max_seq_len, num_splits=s,
+                                                  workspace=ws, stream=self.launch_stream)
+                    if append:
+                        # The new token's rows are the ones already at key L - 1.
+                        kn = torch.stack([p.k_logical[i][int(p.seq_lens[i]) - 1]
+                                          for i in range(p.num_seqs)]).to(dev)
+                        vn = torch.stack([p.v_logical[i][int(p.seq_lens[i]) - 1]
+                                          for i in range(p.num_seqs)]).to(dev)
+                        a = a[:1] + (binding._ptr(kn), binding._ptr(vn)) + a[1:]
+                        self.keep += [kn, vn]
+                    rc.append(("inkling_rel_attn_decode_append" if append
+                               else "inkling_rel_attn_decode", a))
+                    self.keep += [q, k, v, rel, bt, sl, out, ws, dims]
+                    self.kernel_srcs.add(DECODE_KERNEL_SRC)
+                    if r == 0:
+                        self.splits_used.append(s)
+                else:
+                    cu = torch.from_numpy(p.cu_q_lens).to(dev)
+                    a, dims = binding.prefill_args(q, k, v, bt, sl, cu, rel, p.window, p.scale,
+                                                   out, max_q_len=p.max_q_len,
+                                                   max_seq_len=p.max_seq_len,
+                                                   stream=self.launch_stream)
+                    if append:
+                        rows = [(i, pos) for i in range(p.num_seqs)
+                                for pos in range(int(p.seq_lens[i]) - int(p.q_lens[i]),
+                                                 int(p.seq_lens[i]))]
+                        kn = torch.stack([p.k_logical[i][pos] for i, pos in rows]).to(dev)
+                        vn = torch.stack([p.v_logical[i][pos] for i, pos in rows]).to(dev)
+                        a = a[:1] + (binding._ptr(kn), binding._ptr(vn)) + a[1:]
+                        self.keep += [kn, vn]
+                    rc.append(("inkling_rel_attn_prefill_append" if append
+                               else "inkling_rel_attn_prefill", a))
+                    self.keep += [q, k, v, rel, bt, sl, cu, out, dims]
+                    self.kernel_srcs.add(PREFILL_KERNEL_SRC)
+            calls.append(rc)
+        torch.cuda.synchronize()
+        lib = binding.load()
+        self.fns = [[(getattr(lib, n), a) for n, a in rc] for rc in calls]
+        self.step = self._eager
+        if graph:
+            # One eager run per replica on the capture stream (kernel
+            # attributes are set on first use), then one capture per replica.
+            with torch.cuda.stream(self.launch_stream):
+                for r in range(self.replicas):
+                    self._eager(r)
+            self.launch_stream.synchronize()
+            self.graphs = []
+            for r in range(self.replicas):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=self.launch_stream):
+                    self._eager(r)
+                self.graphs.append(g)
+            torch.cuda.synchronize()
+            self.step = lambda i: self.graphs[i % self.replicas].replay()
+
+    def _eager(self, i):
+        from paged_relative_bias_amd import binding
+        for fn, a in self.fns[i % self.replicas]:
+            st = fn(*a)
+            if st != 0:
+                raise binding.InklingError(st, "step")
+
+    def time(self, steps, warmup):
+        import torch
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        # Timed region: K back-to-back steps, HIP events on the launch stream
+        # at its two ends only (an event between launches adds its own gap).
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        e0.record(self.stream)
+        for i in range(steps):
+            self.step(warmup + i)
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        mean_ms = e0.elapsed_time(e1) / steps
+        # Per-step durations, from a separate pass with an event pair per step.
+        n = max(50, min(steps, 200))
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        for i, (a, b) in enumerate(ev):
+            a.record(self.stream)
+            self.step(i)
+            b.record(self.stream)
+        torch.cuda.synchronize()
+        per = np.array([a.elapsed_time(b) for a, b in ev])
+        return {"ms_per_step": 1e3 * wall / steps, "mean_ms": mean_ms,
+                "median_ms": float(np.median(per)), "p10_ms": float(np.percentile(per, 10)),
+                "p90_ms": float(np.percentile(per, 90)), "per_step_n": n}
+
+
+def record_for(name, batch, wl, t, record_name, cpu):
+    median = t["median_ms"]
+    achieved = wl.step_bytes / (median * 1e-3) / 1e9
+    tflops = wl.step_flops / (median * 1e-3) / 1e12
+    peak_tf = BF16_PEAK_TFLOPS if batch.dtype == "bf16" else FP32_PEAK_TFLOPS
+    traffic = traffic_from_profiles(record_name, sorted(wl.kernel_srcs))
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": wl.step_bytes,
+            "algorithmic_flops_per_launch": wl.step_flops,
+            "launch_ms_median": round(median, 5),
+            "launch_ms_p10": round(t["p10_ms"], 5),
+            "launch_ms_p90": round(t["p90_ms"], 5),
+            "launch_ms_mean_back_to_back": round(t["mean_ms"], 5),
+            "launch_note": (f"achieved and frac from the median of {t['per_step_n']} per-step "
+                            "event pairs; the back-to-back mean is the timed region's"),
+            "mfma_tflops": round(tflops, 2),
+            "mfma_peak_tflops": peak_tf,
+            "mfma_frac": round(tflops / peak_tf, 4)}
+    if traffic:
+        roof["traffic_over_algorithmic"] = round(traffic / wl.step_bytes, 3)
+    cfg = {"workload": name, "num_seqs": int(batch.num_seqs), "total_q": int(batch.total_q),
+           "num_q_heads": batch.num_q_heads, "num_kv_heads": batch.num_kv_heads,
+           "head_dim": batch.head_dim, "window": batch.window, "rel_len": batch.rel_len,
+           "block_size": batch.block_size, "seq_lens_sum": int(batch.seq_lens.sum()),
+           "max_seq_len": int(batch.max_seq_len), "num_splits": wl.splits_used or None,
+           "replicas": wl.replicas}
+    return {"value": round(wl.tokens / (t["ms_per_step"] * 1e-3), 1), "unit": "tokens/s",
+            "ms_per_step": round(t["ms_per_step"], 5), "dtype": batch.dtype,
+            "config": cfg, "roofline": roof, "cpu_baseline": cpu}
+
+
+def make_batch_for(gen_name, args, seed):
+    from paged_relative_bias_amd import inputs
+
+    t0 = time.perf_counter()
+    gen = inputs.WORKLOADS[gen_name]
+    batch = gen(seed=seed, batch=args.batch) if args.batch else gen(seed=seed)
+    if args.spike:
+        batch = spike_bias(batch)
+    log(f"generated {gen_name} in {time.perf_counter() - t0:.1f}s: B={batch.num_seqs} "
+        f"total_q={batch.total_q} Hq={batch.num_q_heads} Hkv={batch.num_kv_heads} "
+        f"D={batch.head_dim} W={batch.window} R={batch.rel_len}")
+    return batch
+
+
+def run_record(record_name, batch, splits, args, dev, steps, warmup, cpu):
+    """Time one record on an already generated batch."""
+    import torch
+
+    kind = "global_mixed_split" if record_name == "global_mixed_split" else batch.name
+    wl = Workload(kind, batch, splits=splits, append=args.append, graph=args.graph,
+                  replicas=args.replicas, dev=dev)
+    t = wl.time(steps, warmup)
+    rec = record_for(kind, batch, wl, t, record_name, cpu)
+    rec["config"]["seed"] = args.seed
+    rec["config"]["launch"] = "hip_graph" if args.graph else "eager"
+    rec["config"]["append"] = bool(args.append)
+    rec["config"]["bias_spike"] = bool(args.spike)
+    r = rec["roofline"]
+    log(f"{record_name}: {t['ms_per_step'] * 1e3:.1f} us/step wall; launch median "
+        f"{r['launch_ms_median'] * 1e3:.1f} us (p10 {r['launch_ms_p10'] * 1e3:.1f}, p90 "
+        f"{r['launch_ms_p90'] * 1e3:.1f}, back-to-back mean "
+        f"{r['launch_ms_mean_back_to_back'] * 1e3:.1f}); {r['achieved']:.0f} GB/s = "
+        f"{100 * r['frac']:.1f}% HBM; {r['mfma_tflops']:.1f} TFLOP/s = "
+        f"{100 * r['mfma_frac']:.2f}% MFMA; {rec['value'] / 1e6:.3f} M tokens/s; "
+        f"splits={wl.splits_used} replicas={wl.replicas}")
+    del wl
+    gc.collect()
+    torch.cuda.empty_cache()
+    return rec
+
+
+def baseline(batch, args, budget):
+    if args.no_cpu_baseline:
+        return None
+    cpu = cpu_baseline(batch, budget)
+    log(f"  cpu baseline ({batch.name}): {cpu}")
+    return cpu
 
 
 def main():
@@ -151,10 +412,10 @@ def main():
     # Prefill launches (~0.7 ms) need about 20 ms of back-to-back work before
     # their duration settles; 50 untimed steps cover that for every workload.
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="local_decode",
-                    choices=["local_decode", "global_decode", "local_prefill",
-                             "global_mixed", "global_mixed_split", "tiny_prefill",
-                             "long_global_decode"])
+    ap.add_argument("--workload", default=None, choices=WORKLOAD_CHOICES,
+                    help="time only this workload (default: the headline and every other)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="without --workload: skip the other workloads' records")
     ap.add_argument("--splits", type=int, default=0, help="decode num_splits (0 = library)")
     ap.add_argument("--replicas", type=int, default=0, help="input copies rotated (0 = auto)")
     ap.add_argument("--seed", type=int, default=0)
@@ -165,7 +426,11 @@ def main():
                          "into the cache in the same launch")
     ap.add_argument("--graph", action="store_true",
                     help="capture each replica's step once in a HIP graph and time replays")
+    ap.add_argument("--spike", action="store_true",
+                    help="+60 on every row's distance-0 bias entry (forces the second pass)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0,
+                    help="seconds of oracle work for the headline's CPU baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
@@ -178,7 +443,7 @@ def main():
         sys.exit(2)
 
     import torch
-    from paged_relative_bias_amd import binding, inputs
+    from paged_relative_bias_amd import binding
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -213,183 +478,41 @@ def main():
                           "copy_read_plus_write_gbs": round(gbs, 1)}))
         return
 
-    wl = args.workload
-    split_mixed = wl == "global_mixed_split"
-    gen = inputs.WORKLOADS["global_mixed" if split_mixed else wl]
-    t0 = time.perf_counter()
-    if args.batch and not wl.endswith("decode"):
+    if args.batch and args.workload and not args.workload.endswith("decode"):
         log("--batch applies to the decode workloads only")
         sys.exit(2)
-    batch = gen(seed=args.seed, batch=args.batch) if args.batch else gen(seed=args.seed)
-    log(f"generated {batch.name} in {time.perf_counter() - t0:.1f}s: B={batch.num_seqs} "
-        f"total_q={batch.total_q} Hq={batch.num_q_heads} Hkv={batch.num_kv_heads} "
-        f"D={batch.head_dim} W={batch.window} R={batch.rel_len}")
-    parts = list(inputs.split_mixed(batch)) if split_mixed else [batch]
-    parts = [p for p in parts if p.num_seqs > 0]
-    alg = [algorithmic(p) for p in parts]
-    step_bytes = sum(a["bytes"] for a in alg)
-    if args.append:
-        # k_new and v_new read once, and the same rows written to the cache.
-        step_bytes += 2 * 2 * batch.total_q * batch.num_kv_heads * batch.head_dim * (
-            2 if batch.dtype == "bf16" else 4)
-    step_flops = sum(a["flops"] for a in alg)
-    replicas = args.replicas or max(2, math.ceil(2 * MALL_BYTES / step_bytes) + 1)
-
-    # With --graph the calls are issued on a side stream that is captured;
-    # the replays then run on the current stream.
-    stream = torch.cuda.current_stream()
-    launch_stream = torch.cuda.Stream() if args.graph else stream
-    calls = []       # per replica: list of (fn_name, args)
-    keep = []        # tensors and dims that must stay alive
-    splits_used = []
-    for r in range(replicas):
-        rc = []
-        for p in parts:
-            q = p.q.to(dev)
-            k, v = p.k_cache.to(dev), p.v_cache.to(dev)
-            rel = p.rel_logits.to(dev)
-            bt = torch.from_numpy(p.block_table).to(dev)
-            sl = torch.from_numpy(p.seq_lens).to(dev)
-            out = torch.empty_like(q)
-            if p.is_decode() and wl != "global_mixed":
-                d = binding.dims_for(q, k, bt, rel, num_seqs=p.num_seqs, max_q_len=1,
-                                     max_seq_len=p.max_seq_len)
-                s = args.splits or binding.num_splits(d, p.window, 0)
-                need = binding.decode_workspace_bytes(d, p.window, s)
-                ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev) if need else None
-                a, dims = binding.decode_args(q, k, v, bt, sl, rel, p.window, p.scale, out,
-                                              max_seq_len=p.max_seq_len, num_splits=s,
-                                              workspace=ws, stream=launch_stream)
-                if args.append:
-                    # The new token's rows are the ones already at key L - 1.
-                    kn = torch.stack([p.k_logical[i][int(p.seq_lens[i]) - 1]
-                                      for i in range(p.num_seqs)]).to(dev)
-                    vn = torch.stack([p.v_logical[i][int(p.seq_lens[i]) - 1]
-                                      for i in range(p.num_seqs)]).to(dev)
-                    a = a[:1] + (binding._ptr(kn), binding._ptr(vn)) + a[1:]
-                    keep += [kn, vn]
-                rc.append(("inkling_rel_attn_decode_append" if args.append
-                           else "inkling_rel_attn_decode", a))
-                keep += [q, k, v, rel, bt, sl, out, ws, dims]
-                if r == 0:
-                    splits_used.append(s)
-            else:
-                cu = torch.from_numpy(p.cu_q_lens).to(dev)
-                a, dims = binding.prefill_args(q, k, v, bt, sl, cu, rel, p.window, p.scale,
-                                               out, max_q_len=p.max_q_len,
-                                               max_seq_len=p.max_seq_len, stream=launch_stream)
-                if args.append:
-                    # The new tokens' rows are the ones already at their keys.
-                    rows = [(i, pos) for i in range(p.num_seqs)
-                            for pos in range(int(p.seq_lens[i]) - int(p.q_lens[i]),
-                                             int(p.seq_lens[i]))]
-                    kn = torch.stack([p.k_logical[i][pos] for i, pos in rows]).to(dev)
-                    vn = torch.stack([p.v_logical[i][pos] for i, pos in rows]).to(dev)
-                    a = a[:1] + (binding._ptr(kn), binding._ptr(vn)) + a[1:]
-                    keep += [kn, vn]
-                rc.append(("inkling_rel_attn_prefill_append" if args.append
-                           else "inkling_rel_attn_prefill", a))
-                keep += [q, k, v, rel, bt, sl, cu, out, dims]
-        calls.append(rc)
-    torch.cuda.synchronize()
-    lib = binding.load()
-    fns = [[(getattr(lib, name), a) for name, a in rc] for rc in calls]
-
-    def eager_step(i):
-        for fn, a in fns[i % replicas]:
-            st = fn(*a)
-            if st != 0:
-                raise binding.InklingError(st, "step")
-
-    step = eager_step
-    if args.graph:
-        # One eager run per replica on the capture stream (kernel attributes
-        # are set on first use), then one capture per replica.
-        with torch.cuda.stream(launch_stream):
-            for r in range(replicas):
-                eager_step(r)
-        launch_stream.synchronize()
-        graphs = []
-        for r in range(replicas):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=launch_stream):
-                eager_step(r)
-            graphs.append(g)
-        torch.cuda.synchronize()
-
-        def step(i):
-            graphs[i % replicas].replay()
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    # Timed region: K back-to-back steps, HIP events on the launch stream at
-    # its two ends only (an event between launches would add its own gap).
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    # Mean launch duration over the timed region (includes the short gaps
-    # between back-to-back launches, so it never flatters the kernel).
-    launch_ms = e0.elapsed_time(e1) / args.steps
-    ms_per_step = 1e3 * wall / args.steps
-    # Spread, from a separate untimed pass with an event pair per step.
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(min(args.steps, 50))]
-    for i, (a, b) in enumerate(ev):
-        a.record(stream)
-        step(i)
-        b.record(stream)
-    torch.cuda.synchronize()
-    per = np.array([a.elapsed_time(b) for a, b in ev])  # ms
-    tokens = sum(p.total_q for p in parts)
-    value = tokens / (ms_per_step * 1e-3)
-
-    achieved = step_bytes / (launch_ms * 1e-3) / 1e9
-    tflops = step_flops / (launch_ms * 1e-3) / 1e12
-    kernel_src = (DECODE_KERNEL_SRC if wl in ("local_decode", "global_decode", "long_global_decode")
-                  else PREFILL_KERNEL_SRC)
-    traffic = traffic_from_profiles(wl, kernel_src)
-    peak_tf = BF16_PEAK_TFLOPS if batch.dtype == "bf16" else FP32_PEAK_TFLOPS
-    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
-            "algorithmic_bytes_per_launch": step_bytes,
-            "launch_ms_mean": round(launch_ms, 5),
-            "launch_ms_p10": round(float(np.percentile(per, 10)), 5),
-            "launch_ms_p90": round(float(np.percentile(per, 90)), 5),
-            "launch_note": "mean over the timed region; p10/p90 from a separate per-step pass",
-            "mfma_tflops": round(tflops, 2),
-            "mfma_frac": round(tflops / peak_tf, 4)}
-    log(f"{wl}: {ms_per_step * 1e3:.1f} us/step wall, {launch_ms * 1e3:.1f} us/launch "
-        f"(p10 {roof['launch_ms_p10'] * 1e3:.1f}, p90 {roof['launch_ms_p90'] * 1e3:.1f}); "
-        f"{achieved:.0f} GB/s = {100 * achieved / HBM_PEAK_GBS:.1f}% HBM; "
-        f"{tflops:.1f} TFLOP/s = {100 * tflops / peak_tf:.2f}% MFMA; "
-        f"{value / 1e6:.3f} M tokens/s; replicas={replicas} splits={splits_used}")
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(batch)
-        log(f"cpu baseline: {cpu}")
-
-    cfg = {"workload": wl, "num_seqs": int(batch.num_seqs), "total_q": int(batch.total_q),
-           "num_q_heads": batch.num_q_heads, "num_kv_heads": batch.num_kv_heads,
-           "head_dim": batch.head_dim, "window": batch.window, "rel_len": batch.rel_len,
-           "block_size": batch.block_size, "seq_lens_sum": int(batch.seq_lens.sum()),
-           "max_seq_len": int(batch.max_seq_len), "num_splits": splits_used or None,
-           "replicas": replicas, "seed": args.seed, "launch": "hip_graph" if args.graph else "eager",
-           "append": bool(args.append)}
-    rec = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
-           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": batch.dtype, "data": "synthetic (seeded N(0,1), shuffled page pool)",
-           "config": cfg, "roofline": roof, "cpu_baseline": cpu}
-    print(json.dumps(rec), flush=True)
+    head_name = args.workload or HEADLINE
+    gen_name = "global_mixed" if head_name == "global_mixed_split" else head_name
+    batch = make_batch_for(gen_name, args, args.seed)
+    cpu = baseline(batch, args, args.cpu_budget)
+    rec = run_record(head_name, batch, args.splits, args, dev, args.steps, args.warmup, cpu)
+    line = {"metric": METRIC, "value": rec["value"], "unit": "tokens/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": rec["ms_per_step"],
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": rec["dtype"], "data": "synthetic (seeded N(0,1), shuffled page pool)",
+            "config": rec["config"], "roofline": rec["roofline"],
+            "cpu_baseline": rec["cpu_baseline"]}
+    del batch
+    gc.collect()
+    if args.workload is None and not args.headline_only:
+        # Every other configuration: at most 100 timed steps each and a
+        # shorter oracle sample; one generated batch serves all its records.
+        others = {}
+        for gname, recs in SECONDARY:
+            try:
+                b = make_batch_for(gname, args, args.seed)
+                cpu = baseline(b, args, min(args.cpu_budget, 10.0))
+                for rname, splits in recs:
+                    others[rname] = run_record(rname, b, splits, args, dev,
+                                               min(args.steps, 100), args.warmup, cpu)
+                del b
+            except Exception as e:  # keep the headline and the other records
+                log(f"{gname}: failed: {e!r}")
+                for rname, _ in recs:
+                    others.setdefault(rname, {"error": repr(e)})
+            gc.collect()
+        line["workloads"] = others
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

@@ -44,6 +44,13 @@
  *    entries in [0, num_blocks).  The kernels clamp what they read so that a
  *    violated precondition cannot make them access memory outside the
  *    arguments, but the result is then unspecified.
+ *  - K/V rows that no query of the call can see (keys older than every
+ *    query's window, slots at or past L_b, pages the block table does not
+ *    reference) and rel_logits entries no visible (query, key) pair indexes
+ *    may hold anything, NaN included: they never reach an output.  A
+ *    non-finite K/V row of a key that some query of a sequence sees may make
+ *    other rows of that sequence non-finite as well (their weight for it is
+ *    0, and 0 * NaN is NaN).
  *  - Results are deterministic: the same inputs give bit-identical outputs.
  */
 #ifndef INKLING_REL_ATTN_H
@@ -140,7 +147,8 @@ inkling_status_t inkling_rel_attn_prefill_append(
  *   num_splits 0 = library choice (inkling_rel_attn_num_splits); 1 = one
  *              pass, no merge; at most 128.
  *   workspace  device memory of at least
- *              inkling_rel_attn_decode_workspace_bytes(dims, splits) bytes,
+ *              inkling_rel_attn_decode_workspace_bytes(dims, window,
+ *              num_splits) bytes,
  *              16-byte aligned; may be NULL only when that size is 0.
  *              Contents on entry are ignored; on exit they are unspecified.
  */
@@ -187,14 +195,20 @@ int32_t inkling_rel_attn_num_splits(const inkling_rel_attn_dims_t* dims,
                                     int32_t window, int32_t device);
 
 /* Workspace bytes a decode call with `num_splits` needs (0 when it is 1;
- * num_splits 0 means the library's choice for device 0). */
+ * num_splits 0 means the library's choice for device 0, which depends on
+ * the window as well as the shapes, hence the window argument). */
 size_t inkling_rel_attn_decode_workspace_bytes(
     const inkling_rel_attn_dims_t* dims, int32_t window, int32_t num_splits);
 
 /*
  * Checks that `device` exists and is a gfx950 GPU.  On failure writes a
  * NUL-terminated message naming the device and its architecture into msg
- * (when msg != NULL and msg_len > 0).
+ * (when msg != NULL and msg_len > 0).  This is the up-front support check
+ * of the vLLM page (sections "Purpose" and "Changes"): a device the kernels
+ * were not built for is rejected before any work, with an error that names
+ * it, instead of failing later inside a kernel.  Returns INKLING_OK,
+ * INKLING_ERR_NO_DEVICE, INKLING_ERR_INVALID_ARGUMENT (no such device) or
+ * INKLING_ERR_UNSUPPORTED_DEVICE.
  */
 inkling_status_t inkling_rel_attn_check_device(int32_t device, char* msg,
                                                size_t msg_len);

@@ -6,8 +6,8 @@ torch stream, and raises on a non-OK status.  There is no fallback: if the
 library is missing or the device is not gfx950, calls fail loudly.
 
 Names mirror the C ABI in include/inkling_rel_attn.h:
-    prefill, decode, num_splits, decode_workspace_bytes, check_device,
-    status_string.
+    prefill, prefill_append, decode, decode_append,
+    num_splits, decode_workspace_bytes, check_device, status_string.
 """
 from __future__ import annotations
 

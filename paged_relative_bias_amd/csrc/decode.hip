@@ -49,6 +49,7 @@
 // V^T . P^T.  One split writes the output; otherwise each wave writes its
 // normalised partial and log-sum-exp, and combine_kernel merges them in
 // split order (no atomics).
+#include <mutex>
 #include <type_traits>
 
 #include "device.hpp"
@@ -483,6 +484,14 @@ decode_kernel(const DecodeParams P) {
         issue(tb[(r + DEPTH) % NBUF], t + DEPTH, true, false);
         const int st = C::STAGES > 1 ? (t & 1) : 0;
         if constexpr (NH == 1) wave_lds_fence();
+        if (t == 0 && s_lo < k_lo) {                     // uniform: split 0 only
+          // Keys of the first page before the first visible key: their P is
+          // 0, but a non-finite V row would still turn 0 * V into NaN in
+          // the PV product, so their V rows are staged as zeros.
+#pragma unroll
+          for (int i = 0; i < C::VLD; ++i)
+            if (s_lo + wave * SPW + i * SPI + lane / LPS < k_lo) tb[r].v[i] = make_uint4(0u, 0u, 0u, 0u);
+        }
         stage_tile(tb[r], st);
         if constexpr (NH > 1) wg_lds_barrier(); else wave_lds_fence();
         if (app && t == ntiles - 1) {                    // uniform: holds key L - 1
@@ -598,14 +607,14 @@ size_t decode_lds_t(const DecodeParams& p) {
 
 template <typename T, int D, bool CLAMP, int NH>
 hipError_t launch_decode_c(const DecodeParams& p, hipStream_t stream) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&decode_kernel<T, D, CLAMP, NH>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // Raise the kernel's dynamic LDS limit once per process (thread-safe).
+  static std::once_flag once;
+  static hipError_t attr = hipSuccess;
+  std::call_once(once, [] {
+    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<T, D, CLAMP, NH>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  });
+  if (attr != hipSuccess) return attr;
   const dim3 grid(p.hkv / NH, p.num_splits, p.num_seqs);
   decode_kernel<T, D, CLAMP, NH><<<grid, dim3(64 * NH), decode_lds_t<T, D>(p), stream>>>(p);
   return hipGetLastError();

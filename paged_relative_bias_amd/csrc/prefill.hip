@@ -51,6 +51,7 @@
 // from LDS first, so that their latency runs under the QK MFMAs and the
 // softmax; the hi-term PV MFMAs go out before the lo terms and the row sum
 // are computed, which then run under them.
+#include <mutex>
 #include <type_traits>
 
 #include "device.hpp"
@@ -616,7 +617,12 @@ prefill_kernel(const PrefillParams P) {
       const bool isv = r >= CPR;
       const int ch = isv ? r - CPR : r;
       const int key = pbase + t;
-      const uint64_t page = (uint32_t)pid_lds[(key >> 4) - pg_lo];
+      // The table holds npg pages from pg_lo; with valid metadata every new
+      // key's page is among them (clipped tables only follow from lengths
+      // above max_seq_len, whose result is unspecified: skip the store).
+      const int pi = (key >> 4) - pg_lo;
+      if (pi >= npg) continue;
+      const uint64_t page = (uint32_t)pid_lds[pi];
       const uint64_t dst = page * page_bytes + (uint64_t)(key & 15) * slot_bytes + head_bytes +
                            (uint64_t)ch * 16u;
       const uint64_t src = ((uint64_t)(q0 + t) * P.hkv + g) * D * SZ + (uint64_t)ch * 16u;
@@ -630,6 +636,17 @@ prefill_kernel(const PrefillParams P) {
     int kt = jb & ~15;
     issue(ra, kt, 0);
     commit(ra, 0, kt);
+    if (kt < jb) {                                       // workgroup-uniform
+      // The first page holds keys before the block's first visible key:
+      // their P is 0 for every column, but a non-finite V row would still
+      // turn 0 * V into NaN in the PV product, so their V rows are zeroed.
+      __builtin_amdgcn_s_waitcnt(0);
+      lds_barrier();
+      T* Vs = stage(0) + N * KP;
+      constexpr int VROW = DMA ? D : VP;                   // V row pitch (elements)
+      for (int c = tid; c < (jb - kt) * CPR; c += blockDim.x)
+        *reinterpret_cast<uint4*>(Vs + (c / CPR) * VROW + (c % CPR) * VEC) = make_uint4(0u, 0u, 0u, 0u);
+    }
     lds_barrier();
     while (true) {
       issue(ra, kt + N, 1);
@@ -682,14 +699,14 @@ size_t lds_bytes_t(int waves, int sb_pitch, int pid_cap) {
 template <typename T, int D, bool APPEND>
 hipError_t launch_a(const PrefillParams& p, hipStream_t stream) {
   const size_t lds = lds_bytes_t<T, D>(kPrefillWaves, p.sb_pitch, p.pid_cap);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&prefill_kernel<T, D, APPEND>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // Raise the kernel's dynamic LDS limit once per process (thread-safe).
+  static std::once_flag once;
+  static hipError_t attr = hipSuccess;
+  std::call_once(once, [] {
+    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<T, D, APPEND>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  });
+  if (attr != hipSuccess) return attr;
   const int64_t total = (int64_t)p.nqb * p.num_seqs * p.hkv;
   const int64_t grid = ((total + 7) / 8) * 8;
   prefill_kernel<T, D, APPEND><<<dim3((unsigned)grid), dim3(kPrefillWaves * 64), lds, stream>>>(p);

@@ -20,7 +20,10 @@ Generation recipe (fixed, so every machine draws the same values):
   * block-table rows are padded with -1;
   * with ``poison=True`` every byte the method must never read is NaN:
     unreferenced pages, the slots past ``L_b`` in each sequence's last page,
-    and every ``rel_logits`` entry no visible (query, key) pair indexes.
+    every ``rel_logits`` entry no visible (query, key) pair indexes and
+    (with a window, unless ``poison_stale=False``) the K/V rows of keys older
+    than the window of every query of the sequence.  The NaN values replace
+    drawn ones after all draws, so they never shift the random stream.
 """
 from __future__ import annotations
 
@@ -102,7 +105,7 @@ def make_batch(rng: np.random.Generator, seq_lens, q_lens, *, num_q_heads: int,
                dtype: str = "bf16", block_size: int = BLOCK_SIZE,
                max_blocks_per_seq: int | None = None, spare_pages: int = 64,
                poison: bool = True, scale: float | None = None,
-               name: str = "") -> Batch:
+               name: str = "", poison_stale: bool = True) -> Batch:
     """Lay out one batch given its lengths; draws pages, q, k, v, rel in order."""
     seq_lens = np.asarray(seq_lens, dtype=np.int32).reshape(-1)
     q_lens = np.asarray(q_lens, dtype=np.int32).reshape(-1)
@@ -153,6 +156,14 @@ def make_batch(rng: np.random.Generator, seq_lens, q_lens, *, num_q_heads: int,
         n = pages_per_seq[b]
         if n == 0:
             continue
+        if poison and poison_stale and window > 0 and int(q_lens[b]) > 0:
+            # Keys before the window of the sequence's earliest query.
+            stale = max(0, L - int(q_lens[b]) - int(window) + 1)
+            if stale:
+                kb = kb.clone()
+                vb = vb.clone()
+                kb[:stale] = float("nan")
+                vb[:stale] = float("nan")
         pad = n * bs - L
         if pad:
             kb = torch.cat([kb, torch.full((pad, Hkv, D), fill, dtype=tdt)])
@@ -277,6 +288,45 @@ def long_global_decode(seed: int = 0, batch: int = 4, lo: int = 32768,
                       poison=poison, name="long_global_decode")
 
 
+# The smaller model of the same family (TensorRT-LLM Inkling page, commit
+# list: the Inkling-Small accuracy commit gives 42 layers and hidden size
+# 4096, and no head counts).  Reading: head_dim stays 128, so 32 query heads,
+# and the KV head counts the Architecture section gives for the family (16
+# local, 8 global) are kept, i.e. grouped-query ratios 2:1 and 4:1.
+HQ_SMALL = 32
+
+
+def small_local_decode(seed: int = 0, batch: int = 64, poison: bool = True) -> Batch:
+    """The local decode batch at the smaller model's 32 query heads."""
+    rng = np.random.default_rng(seed)
+    L = rng.integers(1024, MAX_CONTEXT + 1, size=batch)
+    return make_batch(rng, L, np.ones_like(L), num_q_heads=HQ_SMALL,
+                      num_kv_heads=HKV_LOCAL, head_dim=HEAD_DIM,
+                      window=WINDOW_LOCAL, rel_len=WINDOW_LOCAL,
+                      max_blocks_per_seq=MAX_BLOCKS, poison=poison,
+                      name="small_local_decode")
+
+
+def small_global_decode(seed: int = 0, batch: int = 32, poison: bool = True) -> Batch:
+    """The global decode batch at the smaller model's 32 query heads."""
+    rng = np.random.default_rng(seed)
+    L = rng.integers(4096, MAX_CONTEXT + 1, size=batch)
+    return make_batch(rng, L, np.ones_like(L), num_q_heads=HQ_SMALL,
+                      num_kv_heads=HKV_GLOBAL, head_dim=HEAD_DIM, window=0,
+                      rel_len=MAX_CONTEXT, max_blocks_per_seq=MAX_BLOCKS,
+                      poison=poison, name="small_global_decode")
+
+
+def small_local_prefill(seed: int = 0, batch: int = 8, poison: bool = True) -> Batch:
+    """The local varlen prefill batch at the smaller model's 32 query heads."""
+    rng = np.random.default_rng(seed)
+    L = rng.integers(2048, 4096 + 1, size=batch)
+    return make_batch(rng, L, L, num_q_heads=HQ_SMALL, num_kv_heads=HKV_LOCAL,
+                      head_dim=HEAD_DIM, window=WINDOW_LOCAL,
+                      rel_len=WINDOW_LOCAL, max_blocks_per_seq=MAX_BLOCKS,
+                      poison=poison, name="small_local_prefill")
+
+
 WORKLOADS = {
     "tiny_prefill": tiny,
     "local_decode": local_decode,
@@ -284,6 +334,9 @@ WORKLOADS = {
     "local_prefill": local_prefill,
     "global_mixed": global_mixed,
     "long_global_decode": long_global_decode,
+    "small_local_decode": small_local_decode,
+    "small_global_decode": small_global_decode,
+    "small_local_prefill": small_local_prefill,
 }
 
 

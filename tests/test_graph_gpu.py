@@ -47,8 +47,11 @@ LENGTH_STEPS = [
 def _batch(W, R, Hq, Hkv, seed):
     Lmax = np.max(np.array(LENGTH_STEPS), axis=0).tolist()
     rng = np.random.default_rng(seed)
+    # Replays use shorter lengths than the batch is drawn with, so keys
+    # older than the longest lengths' windows stay finite.
     return inputs.make_batch(rng, Lmax, [1] * len(Lmax), num_q_heads=Hq, num_kv_heads=Hkv,
-                             head_dim=128, window=W, rel_len=R, dtype="bf16")
+                             head_dim=128, window=W, rel_len=R, dtype="bf16",
+                             poison_stale=False)
 
 
 def _permute_pages(d: U.Dev, b, seed):

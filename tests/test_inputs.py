@@ -6,17 +6,23 @@ from paged_relative_bias_amd import inputs
 
 
 def test_pages_hold_logical_keys_and_poison_elsewhere():
+    W = 6
     b = inputs.make_batch(np.random.default_rng(0), [37, 5, 16], [3, 5, 1],
-                          num_q_heads=4, num_kv_heads=2, head_dim=8, window=6,
+                          num_q_heads=4, num_kv_heads=2, head_dim=8, window=W,
                           rel_len=8, dtype="bf16", spare_pages=5)
     used = set()
     for s in range(b.num_seqs):
-        L = int(b.seq_lens[s])
+        L, n = int(b.seq_lens[s]), int(b.q_lens[s])
         npg = (L + 15) // 16
         assert np.all(b.block_table[s, npg:] == -1)
+        stale = max(0, L - n - W + 1)      # keys older than every query's window
         for j in range(L):
             blk = int(b.block_table[s, j // 16])
             used.add(blk)
+            if j < stale:
+                assert torch.isnan(b.k_cache[blk, j % 16].float()).all()
+                assert torch.isnan(b.v_cache[blk, j % 16].float()).all()
+                continue
             assert torch.equal(b.k_cache[blk, j % 16], b.k_logical[s][j])
             assert torch.equal(b.v_cache[blk, j % 16], b.v_logical[s][j])
         last = int(b.block_table[s, npg - 1])
