@@ -160,6 +160,30 @@ inkling_status_t inkling_rel_attn_decode(
     const inkling_rel_attn_dims_t* dims, void* stream);
 
 /*
+ * The same decode as inkling_rel_attn_decode, for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid allocation): it takes no workspace and calls no
+ * allocating routine.  The split partials go to a buffer the library holds
+ * on each GPU it runs on (a 32 MiB device array, kept until the process
+ * ends), whose address is looked up on the first call on that GPU.
+ *   - A call whose split workspace, inkling_rel_attn_decode_workspace_bytes(
+ *     dims, window, num_splits), exceeds 32 MiB returns
+ *     INKLING_ERR_WORKSPACE_TOO_SMALL and launches nothing (use
+ *     inkling_rel_attn_decode with a caller workspace, or fewer splits).
+ *   - Every call on one GPU shares that buffer: calls that overlap in time
+ *     on one GPU (on different streams, or from several threads without
+ *     ordering) race and give unspecified results.  Calls ordered on one
+ *     stream are safe; nothing in it needs to start at zero.
+ *   - No device is current: INKLING_ERR_NO_DEVICE.  Other arguments, outputs
+ *     and errors as inkling_rel_attn_decode.
+ */
+inkling_status_t inkling_rel_attn_decode_noalloc(
+    const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_table, const int32_t* seq_lens,
+    const void* rel_logits, int32_t window, float scale, int32_t num_splits,
+    void* out, const inkling_rel_attn_dims_t* dims, void* stream);
+
+/*
  * Decode that also appends this step's K/V rows to the cache, in the same
  * launch.  The TensorRT-LLM Inkling page's pull request (commit list, the
  * clean-up of the attention op's arguments) shows an attention op that

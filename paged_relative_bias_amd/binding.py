@@ -6,7 +6,7 @@ torch stream, and raises on a non-OK status.  There is no fallback: if the
 library is missing or the device is not gfx950, calls fail loudly.
 
 Names mirror the C ABI in include/inkling_rel_attn.h:
-    prefill, prefill_append, decode, decode_append,
+    prefill, prefill_append, decode, decode_append, decode_noalloc,
     num_splits, decode_workspace_bytes, check_device, status_string.
 """
 from __future__ import annotations
@@ -26,6 +26,7 @@ SYMBOLS = (
     "inkling_rel_attn_prefill_append",
     "inkling_rel_attn_decode",
     "inkling_rel_attn_decode_append",
+    "inkling_rel_attn_decode_noalloc",
     "inkling_rel_attn_num_splits",
     "inkling_rel_attn_decode_workspace_bytes",
     "inkling_rel_attn_check_device",
@@ -70,6 +71,8 @@ def load(path: str = LIB_PATH):
     lib.inkling_rel_attn_decode_append.restype = ctypes.c_int
     lib.inkling_rel_attn_decode_append.argtypes = [P, P, P, P, P, P, P, P, I32, F32, I32, P,
                                                    ctypes.c_size_t, P, DP, P]
+    lib.inkling_rel_attn_decode_noalloc.restype = ctypes.c_int
+    lib.inkling_rel_attn_decode_noalloc.argtypes = [P, P, P, P, P, P, I32, F32, I32, P, DP, P]
     lib.inkling_rel_attn_num_splits.restype = I32
     lib.inkling_rel_attn_num_splits.argtypes = [DP, I32, I32]
     lib.inkling_rel_attn_decode_workspace_bytes.restype = ctypes.c_size_t
@@ -198,6 +201,22 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, rel_logits,
         ctypes.byref(dims), _stream(stream))
     if st != OK:
         raise InklingError(st, "inkling_rel_attn_decode")
+
+
+def decode_noalloc(q, k_cache, v_cache, block_table, seq_lens, rel_logits,
+                   window: int, scale: float, out, *, max_seq_len: int,
+                   num_splits: int = 0, stream=None) -> None:
+    """inkling_rel_attn_decode_noalloc on device tensors: the same decode
+    with the library's own per-GPU split buffer (no workspace argument)."""
+    dims = dims_for(q, k_cache, block_table, rel_logits,
+                    num_seqs=seq_lens.shape[0], max_q_len=1,
+                    max_seq_len=max_seq_len)
+    st = load().inkling_rel_attn_decode_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(seq_lens), _ptr(rel_logits), int(window), float(scale),
+        int(num_splits), _ptr(out), ctypes.byref(dims), _stream(stream))
+    if st != OK:
+        raise InklingError(st, "inkling_rel_attn_decode_noalloc")
 
 
 def decode_append(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens,

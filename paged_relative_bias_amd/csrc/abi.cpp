@@ -369,6 +369,36 @@ inkling_status_t inkling_rel_attn_decode(const void* q, const void* k_cache, con
                      window, scale, num_splits, workspace, workspace_bytes, out, dims, stream);
 }
 
+inkling_status_t inkling_rel_attn_decode_noalloc(const void* q, const void* k_cache,
+                                                 const void* v_cache, const int32_t* block_table,
+                                                 const int32_t* seq_lens, const void* rel_logits,
+                                                 int32_t window, float scale, int32_t num_splits,
+                                                 void* out, const inkling_rel_attn_dims_t* dims,
+                                                 void* stream) {
+  // Host-side checks first: nothing here touches a device before the
+  // arguments are known to be valid and the split workspace to fit.
+  inkling_status_t st = check_dims(dims);
+  if (st != INKLING_OK) return st;
+  if (num_splits < 0 || num_splits > kMaxSplits) return INKLING_ERR_INVALID_ARGUMENT;
+  if (dims->num_seqs == 0) return INKLING_OK;
+  if (num_splits > 0 && workspace_for(dims, num_splits) > decode_scratch_bytes())
+    return INKLING_ERR_WORKSPACE_TOO_SMALL;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return INKLING_ERR_NO_DEVICE;
+  }
+  const int32_t splits = num_splits == 0 ? splits_for(dims, window, device_cus(dev)) : num_splits;
+  if (workspace_for(dims, splits) > decode_scratch_bytes()) return INKLING_ERR_WORKSPACE_TOO_SMALL;
+  void* ws = nullptr;
+  if (decode_scratch(dev, &ws) != hipSuccess || ws == nullptr) {
+    (void)hipGetLastError();
+    return INKLING_ERR_LAUNCH;
+  }
+  return decode_impl(q, nullptr, nullptr, k_cache, v_cache, block_table, seq_lens, rel_logits,
+                     window, scale, splits, ws, decode_scratch_bytes(), out, dims, stream);
+}
+
 inkling_status_t inkling_rel_attn_decode_append(
     const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
     const int32_t* block_table, const int32_t* seq_lens, const void* rel_logits, int32_t window,

@@ -642,7 +642,40 @@ hipError_t launch_combine_t(const CombineParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Device-resident split workspace for callers that cannot allocate
+// (inkling_rel_attn_decode_noalloc): partial outputs and log-sum-exps of the
+// split-KV decode.  Each GPU the library runs on holds its own copy until
+// the process ends; every call on that GPU shares it.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
 }  // namespace
+
+size_t decode_scratch_bytes() { return kScratchBytes; }
+
+hipError_t decode_scratch(int device, void** ptr) {
+  *ptr = nullptr;
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  // Once per device, with that device current: the array's address on that
+  // device (the name itself is only a host-side stand-in).
+  std::call_once(g_scratch_once[device], [device] {
+    int prev = -1;
+    hipError_t e = hipGetDevice(&prev);
+    if (e == hipSuccess && prev != device) e = hipSetDevice(device);
+    void* p = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (prev >= 0 && prev != device) (void)hipSetDevice(prev);
+    g_scratch_err[device] = e;
+    g_scratch_ptr[device] = e == hipSuccess ? p : nullptr;
+  });
+  *ptr = g_scratch_ptr[device];
+  return g_scratch_err[device];
+}
 
 size_t decode_lds_bytes(const DecodeParams& p, int dtype, int head_dim) {
   if (dtype == 0)

@@ -81,5 +81,9 @@ hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim,
 size_t decode_lds_bytes(const DecodeParams& p, int dtype, int head_dim);
 hipError_t launch_combine(const CombineParams& p, int dtype, int head_dim,
                           hipStream_t stream);
+// The library's own split workspace on `device` (a file-scope device array):
+// its size, and its device address, looked up once per device.
+size_t decode_scratch_bytes();
+hipError_t decode_scratch(int device, void** ptr);
 
 }  // namespace ira

@@ -161,3 +161,14 @@ def test_status_strings_and_device_check_without_gpu():
     # In a container without a GPU the check reports it; on a gfx950 box it
     # passes.  Either way it returns a status and a message.
     assert st in (B.OK, 3, 4) and msg
+
+
+def test_noalloc_rejects_oversized_split_workspace_without_a_device():
+    """The no-allocation decode refuses, before touching any device, a call
+    whose split partials would not fit the library's 32 MiB buffer."""
+    d = _dims(num_seqs=64, total_q=64, num_kv_heads=8, rel_len=8192)
+    st = B.load().inkling_rel_attn_decode_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0.088,
+                                                  128, FAKE, ctypes.byref(d), None)
+    assert st == 5   # INKLING_ERR_WORKSPACE_TOO_SMALL
+    assert B.decode_workspace_bytes(d, 0, 128) > 32 << 20
+    assert B.decode_workspace_bytes(d, 0, 8) <= 32 << 20
