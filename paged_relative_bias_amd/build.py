@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libinkling_rel_attn.so")
-SOURCES = ["abi.cpp", "prefill.hip", "decode.hip"]
+SOURCES = ["abi.cpp", "prefill.hip", "prefill_bf16.hip", "decode.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -223,7 +223,12 @@ inkling_status_t prefill_impl(const void* q, const void* k_new, const void* v_ne
   // Pages a workgroup's key range can touch.
   const int64_t span = window > 0 ? (int64_t)p.bq + window - 1 : (int64_t)dims->max_seq_len;
   p.pid_cap = (int32_t)std::min<int64_t>(dims->max_blocks_per_seq, (span + 15) / 16 + 2);
-  if (prefill_lds_bytes(dims->dtype, dims->head_dim, waves, p.sb_pitch, p.pid_cap) > 160 * 1024)
+  // bf16 with head_dim 128 and no append runs the specialised kernel.
+  const bool bf16_fast = dims->dtype == INKLING_DTYPE_BF16 && dims->head_dim == 128 &&
+                         k_new == nullptr;
+  if ((bf16_fast ? prefill_bf16_lds_bytes(p.pid_cap)
+                 : prefill_lds_bytes(dims->dtype, dims->head_dim, waves, p.sb_pitch, p.pid_cap)) >
+      160 * 1024)
     return INKLING_ERR_UNSUPPORTED;
   // 32-bit buffer offsets: one page, and the bias rows of one query block.
   if ((int64_t)16 * dims->num_kv_heads * dims->head_dim * (int64_t)esz >= (1LL << 31) ||
@@ -231,8 +236,9 @@ inkling_status_t prefill_impl(const void* q, const void* k_new, const void* v_ne
     return INKLING_ERR_UNSUPPORTED;
   if ((int64_t)p.nqb * dims->num_seqs * dims->num_kv_heads >= (1LL << 31))
     return INKLING_ERR_UNSUPPORTED;
-  const hipError_t e = launch_prefill(p, dims->dtype, dims->head_dim,
-                                      static_cast<hipStream_t>(stream));
+  const hipError_t e = bf16_fast ? launch_prefill_bf16(p, static_cast<hipStream_t>(stream))
+                                 : launch_prefill(p, dims->dtype, dims->head_dim,
+                                                  static_cast<hipStream_t>(stream));
   return e == hipSuccess ? INKLING_OK : INKLING_ERR_LAUNCH;
 }
 

@@ -1,0 +1,538 @@
+// Varlen prefill for bf16 with head_dim 128 (the serving shapes): relative-
+// bias attention over a paged KV cache on gfx950.
+//
+// Operation (TensorRT-LLM Inkling page, section "Architecture"): logits are
+// scale * q.k plus a learned bias indexed by (query token, head, distance),
+// masked to the causal prefix or to a sliding window, softmax over keys,
+// weighted sum of values.  The paged prefill kernel of the same page
+// (section "Implementation") is the prior art; this is a gfx950 design.
+//
+// Work decomposition and columns are those of the generic prefill kernel:
+// one workgroup per (block of bq query tokens, sequence b, KV head g) on an
+// XCD-remapped 1-D grid; the 4 waves' 128 MFMA columns are (query head in
+// group, token) pairs, token-major, 32 per wave.  Key tiles of 32 keys sweep
+// the union of the block's visible ranges through two LDS stages; per wave
+// and tile S^T = K . Q^T (32x32x16 bf16 MFMA), x = scale * S + bias, a
+// softmax against a fixed per-column reference (the column's max in its
+// first tile with a visible key; a second pass with the exact max in the
+// rare case a later logit exceeds it by more than kOver), and O^T += V^T .
+// P^T with P as two bf16 terms (hi = RNE(P), lo = RNE(P - hi)).
+//
+// What differs from the generic kernel:
+//   * Key order inside a tile.  LDS row r of a tile holds key
+//     kperm(r) = 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3).  The 32x32
+//     MFMA puts S^T rows 8k + 4u + j (k < 4, j < 4) in lane half u, so with
+//     this order lane half u holds keys 16u .. 16u + 15 of the tile, in
+//     order: element i of a lane is key kt + 16u + i.  The contraction of
+//     the PV product runs over LDS rows, so it needs no change; only the
+//     rows' source slots move (wave w's load i fetches slots 4w .. 4w + 3 of
+//     page i of the tile).
+//   * Bias straight into registers.  A lane's 16 elements are 16 consecutive
+//     distances D0 - 15 .. D0 (D0 = p - kt - 16u) of its column's bias row:
+//     9 dwords from the even entry below D0 - 15, loaded one tile ahead into
+//     registers (three buffer loads, no LDS staging, no over-fetch beyond the
+//     one dword of alignment), and each element is one byte permute (its
+//     16 bits into the high half of an fp32) with lane-constant selectors
+//     (the run's start parity is a lane constant).  Tiles where every
+//     distance of the wave is at the clamp (d >= R - 1) use the column's
+//     entry R - 1, read once; tiles whose visible distances straddle the
+//     clamp read each element's clamped entry.
+//   * K and V rows go from HBM straight into LDS (16-byte buffer loads with
+//     the LDS destination) in the bank-conflict-free layout of the generic
+//     kernel: K row r at byte r * 256 + 128 * (r >> 3), 16-byte chunk c at
+//     c ^ (r & 7); V row r at byte r * 256, chunk c at c ^ (4 * (r & 3)).
+#include <mutex>
+
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace ira {
+namespace {
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+// Largest logit excess over the reference (natural units) for which P =
+// exp(x - m_ref) and the running sums stay far from fp32 / bf16 overflow.
+constexpr float kOver = 40.f;
+
+constexpr int kD = 128;                      // head_dim
+constexpr int kN = kPrefillKeys;             // keys per tile (32)
+constexpr uint32_t kKBytes = 8704;           // K region of a stage (32 rows + 3 x 128 B shift)
+constexpr uint32_t kVBytes = 32 * 256;       // V region of a stage
+constexpr uint32_t kStage = kKBytes + kVBytes;
+
+// Workgroup barrier that orders LDS only: in-flight global loads of the
+// issuing waves are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// fp32 value of the bf16 held in bits [15:0] of w.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+prefill_bf16_kernel(const PrefillParams P) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  constexpr uint32_t SZ = 2;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = P.group, bq = P.bq, R = P.rel_len, W = P.window;
+  // A key at distance d is visible when 0 <= d < W (any d >= 0 without a
+  // window): one unsigned compare against wlim.
+  const uint32_t wlim = W > 0 ? (uint32_t)W : 0x80000000u;
+  const int64_t hq = P.hq;
+
+  // XCD-aware work index: workgroup id x runs on XCD x % 8; give each XCD
+  // a contiguous range of work (query block fastest, heaviest first).
+  const int total = P.nqb * P.num_seqs * P.hkv;
+  const int per_xcd = (total + 7) >> 3;
+  const int w = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (w >= total) return;
+  const int qb = P.nqb - 1 - w % P.nqb;
+  const int bg = w / P.nqb;
+  const int b = bg % P.num_seqs, g = bg / P.num_seqs;
+
+  // Sequence metadata, clamped so that no read leaves the arguments.
+  const int q0 = iclamp(P.cu_q_lens[b], 0, P.total_q);
+  const int q1 = iclamp(P.cu_q_lens[b + 1], q0, P.total_q);
+  const int L = iclamp(P.seq_lens[b], 0, P.max_blocks * 16);
+  const int n = imin(q1 - q0, L);
+  const int t0 = qb * bq;
+  if (t0 >= n) return;
+  const int tend = imin(t0 + bq, n);
+  const int pbase = L - n;                                  // position of token 0
+  const int jb = W > 0 ? imax(0, pbase + t0 - W + 1) : 0;   // block's first key
+  const int je = pbase + tend;                              // one past last key
+
+  // This lane's column (query head, token) and lane half.
+  const int col = lane & 31, u = lane >> 5;
+  const int wc = wave * 32 + col;
+  const int hh = wc % G;
+  const int tc = t0 + wc / G;
+  const bool cval = hh < G && tc < tend;
+  const int h = g * G + (hh < G ? hh : 0);
+  const int pc = pbase + tc;
+  // The wave's token range and its visible key range.
+  const int c_lo = wave * 32, c_hi = imin(c_lo + 31, G * bq - 1);
+  const int wt_lo = t0 + c_lo / G;
+  const int wt_hi = imin(t0 + c_hi / G + 1, tend);   // exclusive
+  const bool wact = c_lo < G * bq && wt_lo < tend;
+  const int wjb = W > 0 ? imax(0, pbase + wt_lo - W + 1) : 0;
+  const int wje = pbase + wt_hi;
+
+  // LDS: two stages of (K tile, V tile), the page-id table, one flag per
+  // wave.
+  int* pid_lds = reinterpret_cast<int*>(smem + 2 * kStage);
+  int* ovf_lds = pid_lds + P.pid_cap;
+
+  // Page ids of keys [jb, je).
+  const int pg_lo = jb >> 4;
+  const int npg = imin(((je - 1) >> 4) - pg_lo + 1, P.pid_cap);
+  {
+    const int seq_pages = (L + 15) >> 4;
+    const __amdgpu_buffer_rsrc_t bt_rsrc =
+        make_rsrc(P.block_table + (int64_t)b * P.max_blocks, (uint32_t)seq_pages * 4u);
+    for (int i = tid; i < npg; i += blockDim.x)
+      pid_lds[i] = iclamp((int)bload32(bt_rsrc, (uint32_t)(pg_lo + i) * 4u), 0, P.num_blocks - 1);
+  }
+
+  // Q^T operand (B of the QK MFMA), held for the whole kernel.
+  bf16x8 qop[8];
+  {
+    const bf16* src = static_cast<const bf16*>(P.q) + ((int64_t)(q0 + tc) * hq + h) * kD + 8 * u;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      qop[s] = cval ? *reinterpret_cast<const bf16x8*>(src + 16 * s) : bf16x8{};
+  }
+
+  const uint32_t slot_bytes = (uint32_t)P.hkv * kD * SZ;
+  const uint32_t page_bytes = 16u * slot_bytes;
+  const uint32_t head_bytes = (uint32_t)g * kD * SZ;
+  const char* kg = static_cast<const char*>(P.k);
+  const char* vg = static_cast<const char*>(P.v);
+  // K/V loads.  Wave w's load i writes LDS rows 4 (2w + i) .. + 3 (one 1 KB
+  // block, lane l at bytes 16 l .. 16 l + 15 after M0), which hold keys
+  // 16 i + 4 w + l / 16: slot 4 w + l / 16 of page i of the tile.  Lane l
+  // writes physical chunk l % 16 of its row, so it fetches the logical chunk
+  // the layout puts there.
+  uint32_t k_lane[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = 4 * (2 * wave + i) + (lane >> 4);
+    k_lane[i] = (uint32_t)(4 * wave + (lane >> 4)) * slot_bytes + head_bytes +
+                (uint32_t)((lane & 15) ^ (row & 7)) * 16u;
+  }
+  const uint32_t v_lane = (uint32_t)(4 * wave + (lane >> 4)) * slot_bytes + head_bytes +
+                          (uint32_t)((lane & 15) ^ (4 * (lane >> 4))) * 16u;
+
+  // Bias rows of tokens [t0, tend), all heads: row (t, h') at
+  // ((t - t0) * Hq + h') * R entries after rel_base.
+  const bf16* rel_base = static_cast<const bf16*>(P.rel) + (int64_t)(q0 + t0) * hq * R;
+  const uint32_t rel_bytes = (uint32_t)(tend - t0) * (uint32_t)hq * (uint32_t)R * SZ;
+  const __amdgpu_buffer_rsrc_t rel_rsrc = make_rsrc(rel_base, sgpr_u32(rel_bytes));
+  const uint32_t row_off = (uint32_t)((tc - t0) * (int)hq + h) * (uint32_t)R * SZ;
+  // The lane's run of the tile at kt: entries D0 - 15 .. D0, D0 = pc - kt -
+  // 16u, read as the 9 dwords from even entry ((pc - 16u - 15) & ~1) - kt
+  // (kt is a multiple of 16).  Near the diagonal a run starts up to 63
+  // entries before its row (those elements are masked), so the runs are read
+  // through a descriptor whose base sits kMargin bytes before the block's
+  // bias rows: those bytes belong to earlier token rows of the same tensor.
+  // Where fewer bytes precede the block (the tensor's first rows), a wave
+  // whose runs could start before the descriptor reads its run one dword at
+  // a time: a dword load wholly out of range reads zero, while a 16-byte
+  // load that starts out of range would also drop its in-range part.
+  constexpr uint32_t kMargin = 128;
+  const int64_t before = (int64_t)(q0 + t0) * hq * R * SZ;  // bytes of rel_logits before the block
+  const uint32_t margin = before >= (int64_t)kMargin ? kMargin : (uint32_t)before;
+  const int e_run = (pc - 16 * u - 15) & ~1;
+  const int par = (pc - 16 * u - 15) & 1;
+  // Padding columns read nothing: their offset stays far above any row.
+  const uint32_t b_lane = cval ? margin + row_off + (uint32_t)e_run * SZ : 0xf0000000u;
+  const bool run_by_dword = __builtin_amdgcn_ballot_w64(cval && margin + row_off < kMargin) != 0;
+  // Element 2m + 1 is half `par` of dword 7 - m; element 2m is the high half
+  // of dword 7 - m (par = 0) or the low half of dword 8 - m (par = 1).
+  const uint32_t sel_odd = par ? 0x03020c0cu : 0x01000c0cu;
+  const uint32_t sel_even = par ? 0x05040c0cu : 0x03020c0cu;
+  // The column's entry R - 1, for tiles where every distance is clamped.
+  const float bias_cl = cval ? bf16_lo(bload16(rel_rsrc, row_off + (uint32_t)(R - 1) * SZ)) : 0.f;
+
+  // Tile kinds for this wave (all wave-uniform): the largest distance of the
+  // wave's columns in the tile at kt is (wje - 1) - kt, the largest visible
+  // one that or W - 1, the smallest (pbase + wt_lo) - (kt + 31).  A tile
+  // whose visible distances all lie below R takes the runs; elements at
+  // masked distances >= R read whatever follows their row (or zero past the
+  // buffer) and are discarded.
+  const int vis_cap = W > 0 ? W - 1 : 0x7fffffff;
+  auto unclamped = [&](int kt) { return imin((wje - 1) - kt, vis_cap) <= R - 1; };
+  auto all_clamped = [&](int kt) { return (pbase + wt_lo) - (kt + kN - 1) >= R - 1; };
+  auto wave_tile = [&](int kt) { return wact && kt < wje && kt + kN > wjb; };
+
+  // K/V of the tile at kt into LDS stage st.  The descriptors of the tile's
+  // two pages end at key je (keys past it, and whole tiles past the last,
+  // read zero without traffic).  No control flow around any load.
+  auto issue_kv = [&](int kt, int st) {
+    const int pi0 = imin((kt >> 4) - pg_lo, P.pid_cap - 1);        // >= 0
+    const int pi1 = imin(pi0 + 1, P.pid_cap - 1);
+    const uint64_t page0 = (uint32_t)__builtin_amdgcn_readfirstlane(pid_lds[pi0]);
+    const uint64_t page1 = (uint32_t)__builtin_amdgcn_readfirstlane(pid_lds[pi1]);
+    const int nk = __builtin_amdgcn_readfirstlane(je - kt);
+    const uint32_t n0 = sgpr_u32((uint32_t)(nk <= 0 ? 0 : (nk >= 16 ? 16 : nk)) * slot_bytes);
+    const uint32_t n1 = sgpr_u32((uint32_t)(nk <= 16 ? 0 : (nk >= 32 ? 16 : nk - 16)) * slot_bytes);
+    const __amdgpu_buffer_rsrc_t rk0 =
+        make_rsrc(reinterpret_cast<const void*>(sgpr_u64(reinterpret_cast<uint64_t>(kg) + page0 * page_bytes)), n0);
+    const __amdgpu_buffer_rsrc_t rk1 =
+        make_rsrc(reinterpret_cast<const void*>(sgpr_u64(reinterpret_cast<uint64_t>(kg) + page1 * page_bytes)), n1);
+    const __amdgpu_buffer_rsrc_t rv0 =
+        make_rsrc(reinterpret_cast<const void*>(sgpr_u64(reinterpret_cast<uint64_t>(vg) + page0 * page_bytes)), n0);
+    const __amdgpu_buffer_rsrc_t rv1 =
+        make_rsrc(reinterpret_cast<const void*>(sgpr_u64(reinterpret_cast<uint64_t>(vg) + page1 * page_bytes)), n1);
+    // Block kb = 2 w + i: K at kb * 1024 + 128 * (kb >> 1), V at kKBytes +
+    // kb * 1024.  The compiler does not see these loads; every wait for them
+    // is explicit, and nothing else in the kernel uses M0.
+    const uint32_t sl = sgpr_u32((uint32_t)st * kStage);
+    const uint32_t kl0 = sgpr_u32(sl + (uint32_t)(2 * wave) * 1024u + 128u * (uint32_t)wave);
+    const uint32_t kl1 = sgpr_u32(kl0 + 1024u);
+    const uint32_t vl0 = sgpr_u32(sl + kKBytes + (uint32_t)(2 * wave) * 1024u);
+    const uint32_t vl1 = sgpr_u32(vl0 + 1024u);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(kl0), "v"(k_lane[0]), "s"(rk0) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(vl0), "v"(v_lane), "s"(rv0) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(kl1), "v"(k_lane[1]), "s"(rk1) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(vl1), "v"(v_lane), "s"(rv1) : "memory", "m0");
+#pragma clang diagnostic pop
+  };
+
+  // The lane's bias run of the tile at kt (fast tiles only; other tiles,
+  // and tiles this wave does not compute, read nothing).
+  struct Run {
+    uint4 a, b;
+    uint32_t c;
+  };
+  const char* run_base = reinterpret_cast<const char*>(rel_base) - margin;
+  auto issue_bias = [&](Run& r, int kt) {
+    const bool fast = wave_tile(kt) && unclamped(kt);      // wave-uniform
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(run_base, sgpr_u32(fast ? rel_bytes + margin : 0u));
+    // The offset is kept an opaque register value: otherwise the compiler
+    // folds the step between tiles into the instructions' unsigned offset
+    // fields, and a register value that wraps below zero while the true
+    // offset does not would read as out of range.  On the 16-byte path the
+    // offset is at least 2 (see kMargin), so its +16 and +32 never wrap.
+    uint32_t off = b_lane - (uint32_t)kt * SZ;
+    asm volatile("" : "+v"(off));
+    // Runs that reach past their row (masked distances >= R) could run past
+    // the end of the buffer on the block's last rows: those waves also read
+    // one dword at a time, so that no 16-byte load straddles the end.
+    bool by_dword = run_by_dword;
+    if (fast && (wje - 1) - kt > R - 1)                    // wave-uniform
+      by_dword = by_dword || __builtin_amdgcn_ballot_w64(
+                                 cval && (int64_t)row_off + 2 * ((wje - 1) - kt + 3) >=
+                                             (int64_t)rel_bytes) != 0;
+    if (by_dword) {                                        // wave-uniform, rare
+      // Each dword's offset is its own opaque register value, so that the
+      // compiler can neither merge the loads into 16-byte ones nor fold
+      // parts of the offsets into the offset fields.
+      uint32_t o[9];
+#pragma unroll
+      for (int k = 0; k < 9; ++k) {
+        o[k] = off + 4u * k;
+        asm volatile("" : "+v"(o[k]));
+      }
+      r.a = make_uint4(bload32(rr, o[0]), bload32(rr, o[1]), bload32(rr, o[2]), bload32(rr, o[3]));
+      r.b = make_uint4(bload32(rr, o[4]), bload32(rr, o[5]), bload32(rr, o[6]), bload32(rr, o[7]));
+      r.c = bload32(rr, o[8]);
+    } else {
+      r.a = bload128(rr, off);
+      r.b = bload128(rr, off + 16u);
+      r.c = bload32(rr, off + 32u);
+    }
+  };
+
+  f32x16 acc[kD / 32];
+#pragma unroll
+  for (int dt = 0; dt < kD / 32; ++dt) acc[dt] = f32x16{};
+  // Softmax reference of the column: the max of its logits in the first
+  // tile where it has a visible key (the two lanes of a column agree on it).
+  // Later logits may exceed it; P = exp(x - m_ref) stays finite while they
+  // exceed it by less than kOver, which a running check confirms; if not,
+  // the workgroup streams its keys again with m_ref = the true column max.
+  float m_ref = kNegInf;
+  float l_run = 0.f;
+  float m_all = kNegInf;        // running max of this lane's logits
+  bool second_pass = false;     // workgroup-uniform
+  uint64_t over = 0;            // lanes that saw x > m_ref + kOver
+
+  // ---- compute one tile from LDS stage st ----------------------------------
+  auto compute = [&](int kt, int st, const Run& run) {
+    if (!wave_tile(kt)) return;                           // wave-uniform
+    const bf16* Ks = reinterpret_cast<const bf16*>(smem + (size_t)st * kStage);
+    const bf16* Vs = reinterpret_cast<const bf16*>(smem + (size_t)st * kStage + kKBytes);
+    const int D0 = pc - kt - 16 * u;                       // distance of element 0
+    // V^T operands of this tile, read first so that their LDS latency runs
+    // under the QK product and the softmax.  Operand ks covers the S^T rows
+    // of elements 8 ks .. 8 ks + 7: rows 4u + e (e < 4) and 8 + 4u + e - 4 of
+    // the 16-row half ks.  The 16-lane groups of a transposed read cover
+    // columns d0 .. d0 + 15: lane jj points at row 4u + jj / 4, columns
+    // d0 + 4 (jj % 4) .. + 3.  Rows 4u + jj / 4 (+ 8, + 16) share r & 3 =
+    // jj / 4, so d-block dt of the lane's columns starts 32 (dt ^ (jj / 4))
+    // elements into the row.
+    bf16x8 va[kD / 32][2];
+    {
+      const int jj = lane & 15;
+      const int dgrp = (lane >> 4) & 1;
+      const bf16* vbase = Vs + (4 * u + (jj >> 2)) * kD + 8 * (2 * dgrp + ((jj & 3) >> 1)) +
+                          4 * (jj & 1);
+#pragma unroll
+      for (int dt = 0; dt < kD / 32; ++dt) {
+        const bf16* vb = vbase + 32 * (dt ^ (jj >> 2));
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(vb + (16 * ks) * kD));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(vb + (16 * ks + 8) * kD));
+          const i16x8 a16 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          va[dt][ks] = __builtin_bit_cast(bf16x8, a16);
+        }
+      }
+    }
+    // S^T = K . Q^T.  Logical chunk 2 s + u of row col sits at chunk
+    // (2 s + u) ^ (col & 7) = 2 ((s & 3) ^ y) + z + 8 (s >> 2).
+    f32x16 s = f32x16{};
+    {
+      const int y = (col & 7) >> 1, z = u ^ (col & 1);
+      const bf16* krow = Ks + col * kD + 64 * (col >> 3) + 8 * z;
+#pragma unroll
+      for (int s2 = 0; s2 < 8; ++s2)
+        s = mfma32(*reinterpret_cast<const bf16x8*>(krow + 16 * ((s2 & 3) ^ y) + 64 * (s2 >> 2)),
+                   qop[s2], s);
+    }
+    // Element i (S^T row 8 (i / 4) + 4u + i % 4 = key kt + 16u + i) sits at
+    // distance D0 - i.
+    float bias[16];
+    if (unclamped(kt)) {                                  // wave-uniform
+      const uint32_t dw[9] = {run.a.x, run.a.y, run.a.z, run.a.w,
+                              run.b.x, run.b.y, run.b.z, run.b.w, run.c};
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        bias[2 * m + 1] = __builtin_bit_cast(float, __builtin_amdgcn_perm(dw[7 - m], dw[7 - m], sel_odd));
+        bias[2 * m] = __builtin_bit_cast(float, __builtin_amdgcn_perm(dw[8 - m], dw[7 - m], sel_even));
+      }
+    } else if (all_clamped(kt)) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) bias[i] = bias_cl;
+    } else {
+      // The tile straddles the clamp: every element's own clamped entry.
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int e = iclamp(D0 - i, 0, R - 1);
+        bias[i] = cval ? bf16_lo(bload16(rel_rsrc, row_off + (uint32_t)e * SZ)) : 0.f;
+      }
+    }
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = fmaf(s[i], P.scale, bias[i]);
+    // Mask by select on tiles that cross the window or causal boundary.
+    const bool full = (W <= 0 || (wje - 1) - kt < W) && (pbase + wt_lo) - (kt + kN - 1) >= 0;
+    if (!full) {                                          // wave-uniform
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[i] = (uint32_t)(D0 - i) < wlim ? x[i] : kNegInf;
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, x[i]);
+    // Columns still without a reference take this tile's column max (which
+    // stays -inf while the column has no visible key: then P = 0).
+    if (!second_pass && __builtin_amdgcn_ballot_w64(m_ref == kNegInf)) {
+      const float mc = fmaxf(mx, xor_lane(mx, 32));
+      m_ref = m_ref == kNegInf ? mc : m_ref;
+    }
+    m_all = fmaxf(m_all, mx);
+    // Padding columns (no such head or token) see zero q and bias; only real
+    // columns decide on a second pass.
+    over |= __builtin_amdgcn_ballot_w64(cval && mx > m_ref + kOver);
+    const float mb = m_ref == kNegInf ? 0.f : m_ref * kLog2e;
+    // P enters the PV product as two bf16 terms, hi = RNE(P) and lo =
+    // RNE(P - hi), whose sum is P to 2^-17 relative; a single bf16 P would
+    // move an output by up to 2^-8 of the spread of V.  Exponentials and the
+    // hi terms first; the lo terms and the row sum are computed while the
+    // hi-term MFMAs run.
+    float pv[16];
+    uint32_t hw[8];
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      pv[i] = fast_exp2(fmaf(x[i], kLog2e, -mb));
+      pv[i + 1] = fast_exp2(fmaf(x[i + 1], kLog2e, -mb));
+      hw[i >> 1] = bf16x2_hi(pv[i], pv[i + 1]);
+    }
+    bf16x8 ph[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      ph[ks] = __builtin_bit_cast(bf16x8, u32x4{hw[4 * ks], hw[4 * ks + 1], hw[4 * ks + 2],
+                                                hw[4 * ks + 3]});
+#pragma unroll
+    for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) acc[dt] = mfma32(va[dt][ks], ph[ks], acc[dt]);
+    uint32_t lw[8];
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      lw[i >> 1] = bf16x2_lo(pv[i], pv[i + 1], hw[i >> 1]);
+      l_run += pv[i];
+      l_run += pv[i + 1];
+    }
+    bf16x8 pl[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      pl[ks] = __builtin_bit_cast(bf16x8, u32x4{lw[4 * ks], lw[4 * ks + 1], lw[4 * ks + 2],
+                                                lw[4 * ks + 3]});
+#pragma unroll
+    for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) acc[dt] = mfma32(va[dt][ks], pl[ks], acc[dt]);
+  };
+
+  // ---- software pipeline over key tiles ------------------------------------
+  // At the top of each step tile kt sits in LDS stage st with its bias run
+  // in `cur`; tile kt + N's K/V are issued into the other stage and its bias
+  // run into `nxt`, and both land while tile kt is computed.  A wait for
+  // every load, a copy of `nxt` into `cur` and one barrier then hand the
+  // stages over.  No load ever writes the registers compute() reads, so the
+  // compiler places no wait for in-flight loads inside a tile.  Loads past
+  // the last tile read nothing, so no load sits under control flow.
+  Run cur, nxt;
+  while (true) {
+    lds_barrier();                                       // page ids ready
+    int kt = jb & ~15;
+    int st = 0;
+    issue_kv(kt, 0);
+    issue_bias(nxt, kt);
+    __builtin_amdgcn_s_waitcnt(0);
+    cur = nxt;
+    if (kt < jb) {                                       // workgroup-uniform
+      // The first page holds keys before the block's first visible key:
+      // their P is 0 for every column, but a non-finite V row would still
+      // turn 0 * V into NaN in the PV product, so their V rows are zeroed.
+      // Key k < 16 of the tile sits in LDS row 8 (k >> 2) + (k & 3).
+      lds_barrier();
+      unsigned char* Vs = smem + kKBytes;
+      for (int c = tid; c < (jb - kt) * 16; c += blockDim.x) {
+        const int k = c >> 4;
+        *reinterpret_cast<uint4*>(Vs + (8 * (k >> 2) + (k & 3)) * 256 + (c & 15) * 16) =
+            make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+    lds_barrier();
+    while (true) {
+      issue_kv(kt + kN, st ^ 1);
+      issue_bias(nxt, kt + kN);
+      compute(kt, st, cur);
+      if (kt + kN >= je) break;                          // workgroup-uniform
+      __builtin_amdgcn_s_waitcnt(0);
+      cur = nxt;
+      lds_barrier();
+      kt += kN;
+      st ^= 1;
+    }
+    // Prefetches past the last tile may be outstanding: drain them, and
+    // decide workgroup-wide whether a second pass is needed.
+    __builtin_amdgcn_s_waitcnt(0);
+    if (lane == 0) ovf_lds[wave] = over != 0 ? 1 : 0;
+    lds_barrier();
+    const bool any = (ovf_lds[0] | ovf_lds[1] | ovf_lds[2] | ovf_lds[3]) != 0;
+    if (second_pass || !any) break;
+    // Rare: some logit exceeded its column's reference by more than kOver.
+    second_pass = true;
+    m_ref = fmaxf(m_all, xor_lane(m_all, 32));
+#pragma unroll
+    for (int dt = 0; dt < kD / 32; ++dt) acc[dt] = f32x16{};
+    l_run = 0.f;
+  }
+
+  if (!wact) return;
+  const float lt = l_run + xor_lane(l_run, 32);
+  if (!cval) return;
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  bf16* dst = static_cast<bf16*>(P.out) + ((int64_t)(q0 + tc) * hq + h) * kD;
+#pragma unroll
+  for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const bf16x4 v = {from_f32<bf16>(acc[dt][4 * q4] * inv), from_f32<bf16>(acc[dt][4 * q4 + 1] * inv),
+                        from_f32<bf16>(acc[dt][4 * q4 + 2] * inv),
+                        from_f32<bf16>(acc[dt][4 * q4 + 3] * inv)};
+      *reinterpret_cast<bf16x4*>(dst + 32 * dt + 8 * q4 + 4 * u) = v;
+    }
+}
+
+}  // namespace
+
+size_t prefill_bf16_lds_bytes(int pid_cap) {
+  return 2 * (size_t)kStage + (size_t)pid_cap * 4 + (size_t)kPrefillWaves * 4;
+}
+
+hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) {
+  // Raise the kernel's dynamic LDS limit once per process (thread-safe).
+  static std::once_flag once;
+  static hipError_t attr = hipSuccess;
+  std::call_once(once, [] {
+    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_bf16_kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  });
+  if (attr != hipSuccess) return attr;
+  const int64_t total = (int64_t)p.nqb * p.num_seqs * p.hkv;
+  const int64_t grid = ((total + 7) / 8) * 8;
+  prefill_bf16_kernel<<<dim3((unsigned)grid), dim3(kPrefillWaves * 64),
+                        prefill_bf16_lds_bytes(p.pid_cap), stream>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace ira
