@@ -27,13 +27,16 @@
 //     the PV product runs over LDS rows, so it needs no change; only the
 //     rows' source slots move (wave w's load i fetches slots 4w .. 4w + 3 of
 //     page i of the tile).
-//   * Bias straight into registers.  A lane's 16 elements are 16 consecutive
-//     distances D0 - 15 .. D0 (D0 = p - kt - 16u) of its column's bias row:
-//     9 dwords from the even entry below D0 - 15, loaded one tile ahead into
-//     registers (three buffer loads, no LDS staging, no over-fetch beyond the
-//     one dword of alignment), and each element is one byte permute (its
-//     16 bits into the high half of an fp32) with lane-constant selectors
-//     (the run's start parity is a lane constant).  Tiles where every
+//   * Bias through LDS, two tiles ahead.  For every column the tile needs
+//     one contiguous run of 32 distances of its bias row; the wave copies an
+//     aligned 40-entry window of it (five 16-byte chunks, aligned to the row
+//     so that none straddles a row or the buffer end) straight into its own
+//     LDS region with 16-byte loads that have the LDS destination, into one
+//     of three stages, two tiles ahead of the tile being computed.  A lane
+//     then reads its 16 elements (distances D0 - 15 .. D0, D0 = p - kt - 16u)
+//     as one 32-byte run at a lane-constant offset of its column's window.
+//     Every load of the loop has the LDS destination and is invisible to the
+//     compiler, so all waits are explicit counts.  Tiles where every visible
 //     distance of the wave is at the clamp (d >= R - 1) use the column's
 //     entry R - 1, read once; tiles whose visible distances straddle the
 //     clamp read each element's clamped entry.
@@ -61,6 +64,22 @@ constexpr int kN = kPrefillKeys;             // keys per tile (32)
 constexpr uint32_t kKBytes = 8704;           // K region of a stage (32 rows + 3 x 128 B shift)
 constexpr uint32_t kVBytes = 32 * 256;       // V region of a stage
 constexpr uint32_t kStage = kKBytes + kVBytes;
+// Bias windows: 40 entries (5 chunks of 16 bytes) per column and tile, 160
+// chunks per wave, written by three 1 KB LDS-destination loads (the last
+// one's upper half carries no column and writes zeros).
+constexpr int kWinChunks = 5;
+constexpr uint32_t kBiasWave = 3 * 1024;     // bytes per wave and bias stage
+constexpr int kBiasStages = 3;
+constexpr uint32_t kBiasOff = 2 * kStage;
+constexpr uint32_t kPidOff = kBiasOff + (uint32_t)kBiasStages * kPrefillWaves * kBiasWave;
+
+// Waits until at most N of this wave's vector-memory loads are in flight
+// (the other counters are left alone).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 // Workgroup barrier that orders LDS only: in-flight global loads of the
 // issuing waves are not waited for.
@@ -124,9 +143,9 @@ prefill_bf16_kernel(const PrefillParams P) {
   const int wjb = W > 0 ? imax(0, pbase + wt_lo - W + 1) : 0;
   const int wje = pbase + wt_hi;
 
-  // LDS: two stages of (K tile, V tile), the page-id table, one flag per
-  // wave.
-  int* pid_lds = reinterpret_cast<int*>(smem + 2 * kStage);
+  // LDS: two stages of (K tile, V tile), three stages of the waves' bias
+  // windows, the page-id table, one flag per wave.
+  int* pid_lds = reinterpret_cast<int*>(smem + kPidOff);
   int* ovf_lds = pid_lds + P.pid_cap;
 
   // Page ids of keys [jb, je).
@@ -175,30 +194,36 @@ prefill_bf16_kernel(const PrefillParams P) {
   const uint32_t rel_bytes = (uint32_t)(tend - t0) * (uint32_t)hq * (uint32_t)R * SZ;
   const __amdgpu_buffer_rsrc_t rel_rsrc = make_rsrc(rel_base, sgpr_u32(rel_bytes));
   const uint32_t row_off = (uint32_t)((tc - t0) * (int)hq + h) * (uint32_t)R * SZ;
-  // The lane's run of the tile at kt: entries D0 - 15 .. D0, D0 = pc - kt -
-  // 16u, read as the 9 dwords from even entry ((pc - 16u - 15) & ~1) - kt
-  // (kt is a multiple of 16).  Near the diagonal a run starts up to 63
-  // entries before its row (those elements are masked), so the runs are read
-  // through a descriptor whose base sits kMargin bytes before the block's
-  // bias rows: those bytes belong to earlier token rows of the same tensor.
-  // Where fewer bytes precede the block (the tensor's first rows), a wave
-  // whose runs could start before the descriptor reads its run one dword at
-  // a time: a dword load wholly out of range reads zero, while a 16-byte
-  // load that starts out of range would also drop its in-range part.
-  constexpr uint32_t kMargin = 128;
-  const int64_t before = (int64_t)(q0 + t0) * hq * R * SZ;  // bytes of rel_logits before the block
-  const uint32_t margin = before >= (int64_t)kMargin ? kMargin : (uint32_t)before;
-  const int e_run = (pc - 16 * u - 15) & ~1;
-  const int par = (pc - 16 * u - 15) & 1;
-  // Padding columns read nothing: their offset stays far above any row.
-  const uint32_t b_lane = cval ? margin + row_off + (uint32_t)e_run * SZ : 0xf0000000u;
-  const bool run_by_dword = __builtin_amdgcn_ballot_w64(cval && margin + row_off < kMargin) != 0;
-  // Element 2m + 1 is half `par` of dword 7 - m; element 2m is the high half
-  // of dword 7 - m (par = 0) or the low half of dword 8 - m (par = 1).
-  const uint32_t sel_odd = par ? 0x03020c0cu : 0x01000c0cu;
-  const uint32_t sel_even = par ? 0x05040c0cu : 0x03020c0cu;
+  // Bias window of the tile at kt for a column at position p: entries
+  // [w0, w0 + 40) of its row with w0 = floor_to(p - 31, 8) - kt (kt is a
+  // multiple of 16), which holds distances p - kt - 31 .. p - kt.  LDS load
+  // m of a wave writes chunks 64 m .. 64 m + 63 of its region: chunk c is
+  // part c % 5 of column c / 5's window.  Chunks before or past the buffer
+  // read zero (their distances are masked); chunks of padding columns, and
+  // of the last load's upper half, read nothing.
+  uint32_t b_dma[3];
+#pragma unroll
+  for (int m = 0; m < 3; ++m) {
+    const int c = 64 * m + lane;
+    const int bc = c / kWinChunks, part = c - bc * kWinChunks;
+    const int rc = wave * 32 + bc;
+    const int rh = rc % G, rt = t0 + rc / G;
+    const bool ok = bc < 32 && rh < G && rt < tend;
+    const int w0 = floor_to(pbase + rt - (kN - 1), 8);
+    b_dma[m] = ok ? (uint32_t)((rt - t0) * (int)hq + g * G + rh) * (uint32_t)R * SZ +
+                        (uint32_t)(w0 + 8 * part) * SZ
+                  : 0xfffffff0u;
+  }
+  // The lane's 16 elements: entries D0 - 15 .. D0 of the window, i.e. 32
+  // bytes from entry ((pc - 31) & 7) + 16 (1 - u) of its column's window.
+  const uint32_t b_read = (uint32_t)col * (kWinChunks * 16) +
+                          (uint32_t)(((pc - (kN - 1)) & 7) + 16 * (1 - u)) * SZ;
   // The column's entry R - 1, for tiles where every distance is clamped.
   const float bias_cl = cval ? bf16_lo(bload16(rel_rsrc, row_off + (uint32_t)(R - 1) * SZ)) : 0.f;
+  // Drain the loads the compiler sees (Q, the clamp entry) before the loop:
+  // its own waits count only those, so a later use of them would otherwise
+  // wait for every LDS-destination load in flight.
+  __builtin_amdgcn_s_waitcnt(0);
 
   // Tile kinds for this wave (all wave-uniform): the largest distance of the
   // wave's columns in the tile at kt is (wje - 1) - kt, the largest visible
@@ -251,48 +276,23 @@ prefill_bf16_kernel(const PrefillParams P) {
 #pragma clang diagnostic pop
   };
 
-  // The lane's bias run of the tile at kt (fast tiles only; other tiles,
-  // and tiles this wave does not compute, read nothing).
-  struct Run {
-    uint4 a, b;
-    uint32_t c;
-  };
-  const char* run_base = reinterpret_cast<const char*>(rel_base) - margin;
-  auto issue_bias = [&](Run& r, int kt) {
-    const bool fast = wave_tile(kt) && unclamped(kt);      // wave-uniform
-    const __amdgpu_buffer_rsrc_t rr = make_rsrc(run_base, sgpr_u32(fast ? rel_bytes + margin : 0u));
-    // The offset is kept an opaque register value: otherwise the compiler
-    // folds the step between tiles into the instructions' unsigned offset
-    // fields, and a register value that wraps below zero while the true
-    // offset does not would read as out of range.  On the 16-byte path the
-    // offset is at least 2 (see kMargin), so its +16 and +32 never wrap.
-    uint32_t off = b_lane - (uint32_t)kt * SZ;
-    asm volatile("" : "+v"(off));
-    // Runs that reach past their row (masked distances >= R) could run past
-    // the end of the buffer on the block's last rows: those waves also read
-    // one dword at a time, so that no 16-byte load straddles the end.
-    bool by_dword = run_by_dword;
-    if (fast && (wje - 1) - kt > R - 1)                    // wave-uniform
-      by_dword = by_dword || __builtin_amdgcn_ballot_w64(
-                                 cval && (int64_t)row_off + 2 * ((wje - 1) - kt + 3) >=
-                                             (int64_t)rel_bytes) != 0;
-    if (by_dword) {                                        // wave-uniform, rare
-      // Each dword's offset is its own opaque register value, so that the
-      // compiler can neither merge the loads into 16-byte ones nor fold
-      // parts of the offsets into the offset fields.
-      uint32_t o[9];
+  // Bias windows of the tile at kt into bias stage bs (tiles the wave
+  // computes on the window path; for the others the loads read nothing and
+  // write zeros).
+  auto issue_bias = [&](int kt, int bs) {
+    const bool win = wave_tile(kt) && unclamped(kt);       // wave-uniform
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(rel_base, sgpr_u32(win ? rel_bytes : 0u));
+    const uint32_t bl = sgpr_u32(kBiasOff + (uint32_t)(bs * kPrefillWaves + wave) * kBiasWave);
 #pragma unroll
-      for (int k = 0; k < 9; ++k) {
-        o[k] = off + 4u * k;
-        asm volatile("" : "+v"(o[k]));
-      }
-      r.a = make_uint4(bload32(rr, o[0]), bload32(rr, o[1]), bload32(rr, o[2]), bload32(rr, o[3]));
-      r.b = make_uint4(bload32(rr, o[4]), bload32(rr, o[5]), bload32(rr, o[6]), bload32(rr, o[7]));
-      r.c = bload32(rr, o[8]);
-    } else {
-      r.a = bload128(rr, off);
-      r.b = bload128(rr, off + 16u);
-      r.c = bload32(rr, off + 32u);
+    for (int m = 0; m < 3; ++m) {
+      // Below zero the offset wraps to a large value and reads zero.
+      const uint32_t off = b_dma[m] - (uint32_t)kt * SZ;
+      const uint32_t ml = sgpr_u32(bl + 1024u * (uint32_t)m);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                   :: "s"(ml), "v"(off), "s"(rr) : "memory", "m0");
+#pragma clang diagnostic pop
     }
   };
 
@@ -311,7 +311,7 @@ prefill_bf16_kernel(const PrefillParams P) {
   uint64_t over = 0;            // lanes that saw x > m_ref + kOver
 
   // ---- compute one tile from LDS stage st ----------------------------------
-  auto compute = [&](int kt, int st, const Run& run) {
+  auto compute = [&](int kt, int st, int bs) {
     if (!wave_tile(kt)) return;                           // wave-uniform
     const bf16* Ks = reinterpret_cast<const bf16*>(smem + (size_t)st * kStage);
     const bf16* Vs = reinterpret_cast<const bf16*>(smem + (size_t)st * kStage + kKBytes);
@@ -359,12 +359,19 @@ prefill_bf16_kernel(const PrefillParams P) {
     // distance D0 - i.
     float bias[16];
     if (unclamped(kt)) {                                  // wave-uniform
-      const uint32_t dw[9] = {run.a.x, run.a.y, run.a.z, run.a.w,
-                              run.b.x, run.b.y, run.b.z, run.b.w, run.c};
+      // Halfword m of the lane's 32-byte run is entry D0 - 15 + m, i.e.
+      // element 15 - m.
+      const bf16* run = reinterpret_cast<const bf16*>(
+          smem + kBiasOff + (uint32_t)(bs * kPrefillWaves + wave) * kBiasWave + b_read);
+      uint2 w4[4];
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        bias[2 * m + 1] = __builtin_bit_cast(float, __builtin_amdgcn_perm(dw[7 - m], dw[7 - m], sel_odd));
-        bias[2 * m] = __builtin_bit_cast(float, __builtin_amdgcn_perm(dw[8 - m], dw[7 - m], sel_even));
+      for (int k = 0; k < 4; ++k) __builtin_memcpy(&w4[k], run + 4 * k, 8);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        bias[15 - 4 * k] = bf16_lo(w4[k].x);
+        bias[14 - 4 * k] = __builtin_bit_cast(float, w4[k].x & 0xffff0000u);
+        bias[13 - 4 * k] = bf16_lo(w4[k].y);
+        bias[12 - 4 * k] = __builtin_bit_cast(float, w4[k].y & 0xffff0000u);
       }
     } else if (all_clamped(kt)) {
 #pragma unroll
@@ -441,22 +448,24 @@ prefill_bf16_kernel(const PrefillParams P) {
   };
 
   // ---- software pipeline over key tiles ------------------------------------
-  // At the top of each step tile kt sits in LDS stage st with its bias run
-  // in `cur`; tile kt + N's K/V are issued into the other stage and its bias
-  // run into `nxt`, and both land while tile kt is computed.  A wait for
-  // every load, a copy of `nxt` into `cur` and one barrier then hand the
-  // stages over.  No load ever writes the registers compute() reads, so the
-  // compiler places no wait for in-flight loads inside a tile.  Loads past
-  // the last tile read nothing, so no load sits under control flow.
-  Run cur, nxt;
+  // At the top of each step tile kt sits in K/V stage st and bias stage bs,
+  // the next tile's bias is in flight into the stage after; tile kt + N's
+  // K/V are issued into the other K/V stage and tile kt + 2N's bias windows
+  // into the third bias stage, all while tile kt is computed.  Every wave
+  // issues, per step, 4 K/V loads then 3 bias loads, so waiting until at
+  // most 3 are in flight completes the next tile's K/V and bias and leaves
+  // the one after in flight; one barrier then hands the K/V stage over (each
+  // wave's bias region is its own).  Loads past the last tile read nothing,
+  // so no load sits under control flow.  Nothing the compiler sees is loaded
+  // in the loop outside the rare clamp path, so it adds no waits of its own.
   while (true) {
     lds_barrier();                                       // page ids ready
     int kt = jb & ~15;
-    int st = 0;
+    int st = 0, bs = 0;
     issue_kv(kt, 0);
-    issue_bias(nxt, kt);
-    __builtin_amdgcn_s_waitcnt(0);
-    cur = nxt;
+    issue_bias(kt, 0);
+    issue_bias(kt + kN, 1);
+    wait_vmem<3>();
     if (kt < jb) {                                       // workgroup-uniform
       // The first page holds keys before the block's first visible key:
       // their P is 0 for every column, but a non-finite V row would still
@@ -473,14 +482,14 @@ prefill_bf16_kernel(const PrefillParams P) {
     lds_barrier();
     while (true) {
       issue_kv(kt + kN, st ^ 1);
-      issue_bias(nxt, kt + kN);
-      compute(kt, st, cur);
+      issue_bias(kt + 2 * kN, bs == 0 ? 2 : bs - 1);
+      compute(kt, st, bs);
       if (kt + kN >= je) break;                          // workgroup-uniform
-      __builtin_amdgcn_s_waitcnt(0);
-      cur = nxt;
+      wait_vmem<3>();
       lds_barrier();
       kt += kN;
       st ^= 1;
+      bs = bs == 2 ? 0 : bs + 1;
     }
     // Prefetches past the last tile may be outstanding: drain them, and
     // decide workgroup-wide whether a second pass is needed.
@@ -516,7 +525,7 @@ prefill_bf16_kernel(const PrefillParams P) {
 }  // namespace
 
 size_t prefill_bf16_lds_bytes(int pid_cap) {
-  return 2 * (size_t)kStage + (size_t)pid_cap * 4 + (size_t)kPrefillWaves * 4;
+  return (size_t)kPidOff + (size_t)pid_cap * 4 + (size_t)kPrefillWaves * 4;
 }
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) {
