@@ -42,9 +42,9 @@
 //     with ds_read_tr16_b64.
 // Per tile: S^T[key][head] = K . Q^T (16x16x32 bf16 MFMA); x = scale * S +
 // bias; masking by select only on the first and last tile of the split;
-// softmax against a fixed reference (the column max of the split's first
-// tile) with a second pass over the split, taken by the whole workgroup, in
-// the rare case that a later logit exceeds it by more than kOver; P as the
+// softmax against a per-column reference (the column max of the split's
+// first tile, raised, with the wave's accumulators rescaled in registers,
+// only on a tile where a logit exceeds it by more than kOver); P as the
 // sum of two bf16 terms (hi + lo) with an fp32 row sum; O^T[d][head] +=
 // V^T . P^T.  One split writes the output; otherwise each wave writes its
 // normalised partial and log-sum-exp, and combine_kernel merges them in
@@ -98,7 +98,7 @@ struct Decode {
   static constexpr size_t b_bytes() { return (size_t)BROWS * BW * SZ; }
   // Stage: K of the NH heads, V of the NH heads, then each wave's bias runs.
   static constexpr size_t stage_bytes() { return NH * (k_bytes() + v_bytes() + b_bytes()); }
-  static constexpr size_t fixed_lds() { return STAGES * stage_bytes() + 16; }
+  static constexpr size_t fixed_lds() { return STAGES * stage_bytes(); }
 };
 
 // One wave's loads of a tile: its K and V slots (for all NH heads) and its
@@ -139,9 +139,7 @@ decode_kernel(const DecodeParams P) {
   constexpr uint32_t SZ = sizeof(T);
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   // LDS: STAGES x {K tiles [NH][NK][KP], V tiles [NH][NK][VSP], bias runs
-  // [NH][BROWS][BW]}, the waves' second-pass flags, then the split's
-  // page-id table.
-  int* ovf_lds = reinterpret_cast<int*>(smem + C::STAGES * C::stage_bytes());
+  // [NH][BROWS][BW]}, then the split's page-id table.
   int* pid_lds = reinterpret_cast<int*>(smem + C::fixed_lds());
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -322,16 +320,14 @@ decode_kernel(const DecodeParams P) {
   f32x4 acc[D / 16];
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{};
-  // Softmax reference: the column max of the split's first tile (the four
-  // lanes of a column agree on it).  Later logits may exceed it; P = exp(x -
-  // m_ref) stays finite as long as they exceed it by less than kOver, which
-  // a running check confirms.  If not, the workgroup streams the split a
-  // second time with m_ref = the split's true column max (then no P
-  // exceeds 1).
+  // Softmax reference (the four lanes of a column agree on it): the column
+  // max of the split's first tile, which always holds a visible key.  Later
+  // logits may exceed it; P = exp(x - m_ref) stays far from overflow while
+  // they exceed it by at most kOver.  On a tile where a logit exceeds it by
+  // more, the column's reference becomes that tile's column max and its
+  // accumulators and row sum are multiplied by exp(old - new), in registers
+  // and only on that tile.
   float m_ref = kNegInf, l_run = 0.f;
-  float m_all = kNegInf;        // running max of this lane's logits
-  bool second_pass = false;     // workgroup-uniform
-  uint64_t over = 0;            // lanes that saw x > m_ref + kOver
 
   // Tile t of this wave's head from LDS stage st.
   auto compute = [&](int t, int st) {
@@ -399,12 +395,20 @@ decode_kernel(const DecodeParams P) {
     }
     const float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                            fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-    if (t == 0 && !second_pass) {                        // uniform
-      const float m = fmaxf(mx, xor_lane(mx, 16));
-      m_ref = fmaxf(m, xor_lane(m, 32));
+    // The first tile sets the reference (from -inf: the factor is 0 and the
+    // accumulators are still 0); a logit more than kOver above it raises it.
+    // Padding columns (no such head) never take the branch.
+    if (__builtin_amdgcn_ballot_w64(cval && mx > m_ref + kOver)) {   // wave-uniform, rare
+      const float m4 = fmaxf(mx, xor_lane(mx, 16));
+      const float mc = fmaxf(m4, xor_lane(m4, 32));
+      if (cval && mc > m_ref + kOver) {
+        const float alpha = fast_exp2((m_ref - mc) * kLog2e);
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) acc[dt] *= alpha;
+        l_run *= alpha;
+        m_ref = mc;
+      }
     }
-    m_all = fmaxf(m_all, mx);
-    over |= __builtin_amdgcn_ballot_w64(mx > m_ref + kOver);
     // P = exp(x - m_ref), and O^T += V^T . P^T.
     const float mb = m_ref == kNegInf ? 0.f : m_ref * kLog2e;
     if constexpr (C::kBF16) {
@@ -474,7 +478,7 @@ decode_kernel(const DecodeParams P) {
   // staging it also tells every wave that all have finished computing tile
   // t - 1, whose stage the next tile reuses.
   Tile<T, D, NH> tb[NBUF];
-  while (true) {
+  {
 #pragma unroll
     for (int i = 0; i < DEPTH; ++i) issue(tb[i], i, true, true);
     for (int t0 = 0;; t0 += NBUF) {
@@ -514,27 +518,9 @@ decode_kernel(const DecodeParams P) {
       }
     }
   done:
-    // Loads past the last tile may still be outstanding; draining them here
-    // keeps the compiler's load accounting exact for a second pass.
+    // Loads past the last tile may still be outstanding: drain them before
+    // the wave ends.
     __builtin_amdgcn_s_waitcnt(0);
-    bool any = over != 0;
-    if constexpr (NH > 1) {
-      if (lane == 0) ovf_lds[wave] = any ? 1 : 0;
-      wg_lds_barrier();
-      any = false;
-#pragma unroll
-      for (int w = 0; w < NH; ++w) any |= ovf_lds[w] != 0;
-      // Every wave has read the flags before any can write them again.
-      wg_lds_barrier();
-    }
-    if (second_pass || !any) break;
-    // Rare: some logit exceeded the first tile's max by more than kOver.
-    second_pass = true;
-    const float m = fmaxf(m_all, xor_lane(m_all, 16));
-    m_ref = fmaxf(m, xor_lane(m, 32));
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{};
-    l_run = 0.f;
   }
   l_run += xor_lane(l_run, 16);
   l_run += xor_lane(l_run, 32);

@@ -38,11 +38,10 @@
 //   x = scale * S + bias          mask by select only on boundary tiles
 //   online softmax per column     two lanes per column (l, l ^ 32); the
 //                                 reference max is the column's max in its
-//                                 first tile with a visible key and the
-//                                 accumulators are never rescaled; a
-//                                 workgroup whose real columns see a logit
-//                                 more than kOver above it streams its keys
-//                                 a second time with the exact column max
+//                                 first tile with a visible key, raised
+//                                 (with the column's accumulators rescaled
+//                                 in registers) only on a tile where a
+//                                 logit exceeds it by more than kOver
 //   O^T[d][col] += V^T . P^T      V^T operand from ds_read_tr16_b64, P^T
 //                                 from registers as two bf16 terms (hi =
 //                                 RNE(P), lo = RNE(P - hi)), two MFMAs;
@@ -177,7 +176,6 @@ prefill_kernel(const PrefillParams P) {
   unsigned char* bias_lds = smem + 2 * C::stage_bytes();
   const int sbp = P.sb_pitch;
   int* pid_lds = reinterpret_cast<int*>(bias_lds + (size_t)nw * 2 * 32 * sbp);
-  int* ovf_lds = pid_lds + P.pid_cap;                    // one flag per wave
 
   // Page ids of keys [jb, je).
   const int pg_lo = jb >> 4;
@@ -387,20 +385,19 @@ prefill_kernel(const PrefillParams P) {
   f32x16 acc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
-  // Softmax reference of the column: the max of its logits in the first
-  // tile where it has a visible key (the two lanes of a column agree on it).
-  // Later logits may exceed it; P = exp(x - m_ref) stays finite while they
-  // exceed it by less than kOver, which a running check confirms; if not,
-  // the workgroup streams its keys again with m_ref = the true column max.
+  // Softmax reference of the column (the two lanes of a column agree on it):
+  // the max of its logits in its first tile with a visible key.  Later
+  // logits may exceed it; P = exp(x - m_ref) stays far from overflow while
+  // they exceed it by at most kOver.  On a tile where a logit exceeds it by
+  // more, the column's reference becomes that tile's column max and its
+  // accumulators and row sum are multiplied by exp(old - new), in registers
+  // and only on that tile.
   // Lane constants of compute(): the column's bias window start at kt = 0
   // (tiles start at multiples of 16) and its lane's distance base.
   const int fpc = floor_to(pc - (N - 1), VEC);
   const int pcu = pc - 4 * u;
   float m_ref = kNegInf;
   float l_run = 0.f;
-  float m_all = kNegInf;        // running max of this lane's logits
-  bool second_pass = false;     // workgroup-uniform
-  uint64_t over = 0;            // lanes that saw x > m_ref + kOver
 
   // ---- compute one tile from LDS stage st --------------------------------
   auto compute = [&](int kt, int st) {
@@ -534,16 +531,21 @@ prefill_kernel(const PrefillParams P) {
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, x[i]);
-    // Columns still without a reference take this tile's column max (which
-    // stays -inf while the column has no visible key: then P = 0).
-    if (!second_pass && __builtin_amdgcn_ballot_w64(m_ref == kNegInf)) {
+    // A column's first tile with a visible key sets its reference (from
+    // -inf: the factor is 0 and the accumulators are still 0); a logit more
+    // than kOver above the reference raises it.  A column without a visible
+    // key keeps -inf (then P = 0).  Padding columns (no such head or token)
+    // may see arbitrary staged values and never take the branch.
+    if (__builtin_amdgcn_ballot_w64(cval && mx > m_ref + kOver)) {   // wave-uniform, rare
       const float mc = fmaxf(mx, xor_lane(mx, 32));
-      m_ref = m_ref == kNegInf ? mc : m_ref;
+      if (cval && mc > m_ref + kOver) {
+        const float alpha = fast_exp2((m_ref - mc) * kLog2e);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= alpha;
+        l_run *= alpha;
+        m_ref = mc;
+      }
     }
-    m_all = fmaxf(m_all, mx);
-    // Padding columns (no such head or token) may see arbitrary staged
-    // values; only real columns decide on a second pass.
-    over |= __builtin_amdgcn_ballot_w64(cval && mx > m_ref + kOver);
     const float mb = m_ref == kNegInf ? 0.f : m_ref * kLog2e;
     if constexpr (C::kBF16) {
       // P enters the PV product as two bf16 terms, hi = RNE(P) and lo =
@@ -631,51 +633,39 @@ prefill_kernel(const PrefillParams P) {
     }
   }
   Regs ra;
-  while (true) {
-    lds_barrier();                                       // page ids ready
-    int kt = jb & ~15;
-    issue(ra, kt, 0);
-    commit(ra, 0, kt);
-    if (kt < jb) {                                       // workgroup-uniform
-      // The first page holds keys before the block's first visible key:
-      // their P is 0 for every column, but a non-finite V row would still
-      // turn 0 * V into NaN in the PV product, so their V rows are zeroed.
-      __builtin_amdgcn_s_waitcnt(0);
-      lds_barrier();
-      T* Vs = stage(0) + N * KP;
-      constexpr int VROW = DMA ? D : VP;                   // V row pitch (elements)
-      for (int c = tid; c < (jb - kt) * CPR; c += blockDim.x)
-        *reinterpret_cast<uint4*>(Vs + (c / CPR) * VROW + (c % CPR) * VEC) = make_uint4(0u, 0u, 0u, 0u);
-    }
-    lds_barrier();
-    while (true) {
-      issue(ra, kt + N, 1);
-      compute(kt, 0);
-      if (kt + N >= je) break;                           // workgroup-uniform
-      commit(ra, 1, kt + N);
-      lds_barrier();
-      kt += N;
-      issue(ra, kt + N, 0);
-      compute(kt, 1);
-      if (kt + N >= je) break;
-      commit(ra, 0, kt + N);
-      lds_barrier();
-      kt += N;
-    }
-    // Prefetches past the last tile may be outstanding: drain them, and
-    // decide workgroup-wide whether a second pass is needed.
+  lds_barrier();                                         // page ids ready
+  int kt = jb & ~15;
+  issue(ra, kt, 0);
+  commit(ra, 0, kt);
+  if (kt < jb) {                                         // workgroup-uniform
+    // The first page holds keys before the block's first visible key: their
+    // P is 0 for every column, but a non-finite V row would still turn 0 * V
+    // into NaN in the PV product, so their V rows are zeroed.
     __builtin_amdgcn_s_waitcnt(0);
-    if (lane == 0) ovf_lds[wave] = over != 0 ? 1 : 0;
     lds_barrier();
-    const bool any = (ovf_lds[0] | ovf_lds[1] | ovf_lds[2] | ovf_lds[3]) != 0;
-    if (second_pass || !any) break;
-    // Rare: some logit exceeded its column's reference by more than kOver.
-    second_pass = true;
-    m_ref = fmaxf(m_all, xor_lane(m_all, 32));
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
-    l_run = 0.f;
+    T* Vs = stage(0) + N * KP;
+    constexpr int VROW = DMA ? D : VP;                     // V row pitch (elements)
+    for (int c = tid; c < (jb - kt) * CPR; c += blockDim.x)
+      *reinterpret_cast<uint4*>(Vs + (c / CPR) * VROW + (c % CPR) * VEC) = make_uint4(0u, 0u, 0u, 0u);
   }
+  lds_barrier();
+  while (true) {
+    issue(ra, kt + N, 1);
+    compute(kt, 0);
+    if (kt + N >= je) break;                             // workgroup-uniform
+    commit(ra, 1, kt + N);
+    lds_barrier();
+    kt += N;
+    issue(ra, kt + N, 0);
+    compute(kt, 1);
+    if (kt + N >= je) break;
+    commit(ra, 0, kt + N);
+    lds_barrier();
+    kt += N;
+  }
+  // Prefetches past the last tile may be outstanding: drain them before the
+  // wave ends.
+  __builtin_amdgcn_s_waitcnt(0);
 
   if (!wact) return;
   const float lt = l_run + xor_lane(l_run, 32);
@@ -693,7 +683,7 @@ prefill_kernel(const PrefillParams P) {
 template <typename T, int D>
 size_t lds_bytes_t(int waves, int sb_pitch, int pid_cap) {
   return 2 * Prefill<T, D>::stage_bytes() + (size_t)waves * 2 * 32 * sb_pitch +
-         (size_t)pid_cap * 4 + (size_t)kPrefillWaves * 4;
+         (size_t)pid_cap * 4;
 }
 
 template <typename T, int D, bool APPEND>

@@ -13,10 +13,11 @@
 // group, token) pairs, token-major, 32 per wave.  Key tiles of 32 keys sweep
 // the union of the block's visible ranges through two LDS stages; per wave
 // and tile S^T = K . Q^T (32x32x16 bf16 MFMA), x = scale * S + bias, a
-// softmax against a fixed per-column reference (the column's max in its
-// first tile with a visible key; a second pass with the exact max in the
-// rare case a later logit exceeds it by more than kOver), and O^T += V^T .
-// P^T with P as two bf16 terms (hi = RNE(P), lo = RNE(P - hi)).
+// softmax against a per-column reference (the column's max in its first
+// tile with a visible key, raised, with the accumulators rescaled in
+// registers, only on a tile where some logit exceeds it by more than
+// kOver), and O^T += V^T . P^T with P as two bf16 terms (hi = RNE(P), lo =
+// RNE(P - hi)).
 //
 // What differs from the generic kernel:
 //   * Key order inside a tile.  LDS row r of a tile holds key
@@ -144,9 +145,8 @@ prefill_bf16_kernel(const PrefillParams P) {
   const int wje = pbase + wt_hi;
 
   // LDS: two stages of (K tile, V tile), three stages of the waves' bias
-  // windows, the page-id table, one flag per wave.
+  // windows, the page-id table.
   int* pid_lds = reinterpret_cast<int*>(smem + kPidOff);
-  int* ovf_lds = pid_lds + P.pid_cap;
 
   // Page ids of keys [jb, je).
   const int pg_lo = jb >> 4;
@@ -299,16 +299,16 @@ prefill_bf16_kernel(const PrefillParams P) {
   f32x16 acc[kD / 32];
 #pragma unroll
   for (int dt = 0; dt < kD / 32; ++dt) acc[dt] = f32x16{};
-  // Softmax reference of the column: the max of its logits in the first
-  // tile where it has a visible key (the two lanes of a column agree on it).
-  // Later logits may exceed it; P = exp(x - m_ref) stays finite while they
-  // exceed it by less than kOver, which a running check confirms; if not,
-  // the workgroup streams its keys again with m_ref = the true column max.
+  // Softmax reference of the column (the two lanes of a column agree on it):
+  // the max of its logits in its first tile with a visible key.  Later
+  // logits may exceed it; P = exp(x - m_ref) stays far from overflow while
+  // they exceed it by at most kOver.  On a tile where a logit exceeds it by
+  // more, the column's reference becomes that tile's column max and its
+  // accumulators and row sum are multiplied by exp(old - new), in registers
+  // and only on that tile; the common tile needs neither a cross-lane
+  // exchange nor a rescale.
   float m_ref = kNegInf;
   float l_run = 0.f;
-  float m_all = kNegInf;        // running max of this lane's logits
-  bool second_pass = false;     // workgroup-uniform
-  uint64_t over = 0;            // lanes that saw x > m_ref + kOver
 
   // ---- compute one tile from LDS stage st ----------------------------------
   auto compute = [&](int kt, int st, int bs) {
@@ -396,16 +396,21 @@ prefill_bf16_kernel(const PrefillParams P) {
     float mx = kNegInf;
 #pragma unroll
     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, x[i]);
-    // Columns still without a reference take this tile's column max (which
-    // stays -inf while the column has no visible key: then P = 0).
-    if (!second_pass && __builtin_amdgcn_ballot_w64(m_ref == kNegInf)) {
+    // A column's first tile with a visible key sets its reference (from
+    // -inf: the factor is 0 and the accumulators are still 0); a logit more
+    // than kOver above the reference raises it.  A column without a visible
+    // key keeps -inf (then P = 0).  Padding columns (no such head or token)
+    // never take the branch.
+    if (__builtin_amdgcn_ballot_w64(cval && mx > m_ref + kOver)) {   // wave-uniform, rare
       const float mc = fmaxf(mx, xor_lane(mx, 32));
-      m_ref = m_ref == kNegInf ? mc : m_ref;
+      if (cval && mc > m_ref + kOver) {
+        const float alpha = fast_exp2((m_ref - mc) * kLog2e);
+#pragma unroll
+        for (int dt = 0; dt < kD / 32; ++dt) acc[dt] *= alpha;
+        l_run *= alpha;
+        m_ref = mc;
+      }
     }
-    m_all = fmaxf(m_all, mx);
-    // Padding columns (no such head or token) see zero q and bias; only real
-    // columns decide on a second pass.
-    over |= __builtin_amdgcn_ballot_w64(cval && mx > m_ref + kOver);
     const float mb = m_ref == kNegInf ? 0.f : m_ref * kLog2e;
     // P enters the PV product as two bf16 terms, hi = RNE(P) and lo =
     // RNE(P - hi), whose sum is P to 2^-17 relative; a single bf16 P would
@@ -458,53 +463,41 @@ prefill_bf16_kernel(const PrefillParams P) {
   // wave's bias region is its own).  Loads past the last tile read nothing,
   // so no load sits under control flow.  Nothing the compiler sees is loaded
   // in the loop outside the rare clamp path, so it adds no waits of its own.
-  while (true) {
-    lds_barrier();                                       // page ids ready
-    int kt = jb & ~15;
-    int st = 0, bs = 0;
-    issue_kv(kt, 0);
-    issue_bias(kt, 0);
-    issue_bias(kt + kN, 1);
-    wait_vmem<3>();
-    if (kt < jb) {                                       // workgroup-uniform
-      // The first page holds keys before the block's first visible key:
-      // their P is 0 for every column, but a non-finite V row would still
-      // turn 0 * V into NaN in the PV product, so their V rows are zeroed.
-      // Key k < 16 of the tile sits in LDS row 8 (k >> 2) + (k & 3).
-      lds_barrier();
-      unsigned char* Vs = smem + kKBytes;
-      for (int c = tid; c < (jb - kt) * 16; c += blockDim.x) {
-        const int k = c >> 4;
-        *reinterpret_cast<uint4*>(Vs + (8 * (k >> 2) + (k & 3)) * 256 + (c & 15) * 16) =
-            make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
+  lds_barrier();                                         // page ids ready
+  int kt = jb & ~15;
+  int st = 0, bs = 0;
+  issue_kv(kt, 0);
+  issue_bias(kt, 0);
+  issue_bias(kt + kN, 1);
+  wait_vmem<3>();
+  if (kt < jb) {                                         // workgroup-uniform
+    // The first page holds keys before the block's first visible key: their
+    // P is 0 for every column, but a non-finite V row would still turn 0 * V
+    // into NaN in the PV product, so their V rows are zeroed.  Key k < 16 of
+    // the tile sits in LDS row 8 (k >> 2) + (k & 3).
     lds_barrier();
-    while (true) {
-      issue_kv(kt + kN, st ^ 1);
-      issue_bias(kt + 2 * kN, bs == 0 ? 2 : bs - 1);
-      compute(kt, st, bs);
-      if (kt + kN >= je) break;                          // workgroup-uniform
-      wait_vmem<3>();
-      lds_barrier();
-      kt += kN;
-      st ^= 1;
-      bs = bs == 2 ? 0 : bs + 1;
+    unsigned char* Vs = smem + kKBytes;
+    for (int c = tid; c < (jb - kt) * 16; c += blockDim.x) {
+      const int k = c >> 4;
+      *reinterpret_cast<uint4*>(Vs + (8 * (k >> 2) + (k & 3)) * 256 + (c & 15) * 16) =
+          make_uint4(0u, 0u, 0u, 0u);
     }
-    // Prefetches past the last tile may be outstanding: drain them, and
-    // decide workgroup-wide whether a second pass is needed.
-    __builtin_amdgcn_s_waitcnt(0);
-    if (lane == 0) ovf_lds[wave] = over != 0 ? 1 : 0;
-    lds_barrier();
-    const bool any = (ovf_lds[0] | ovf_lds[1] | ovf_lds[2] | ovf_lds[3]) != 0;
-    if (second_pass || !any) break;
-    // Rare: some logit exceeded its column's reference by more than kOver.
-    second_pass = true;
-    m_ref = fmaxf(m_all, xor_lane(m_all, 32));
-#pragma unroll
-    for (int dt = 0; dt < kD / 32; ++dt) acc[dt] = f32x16{};
-    l_run = 0.f;
   }
+  lds_barrier();
+  while (true) {
+    issue_kv(kt + kN, st ^ 1);
+    issue_bias(kt + 2 * kN, bs == 0 ? 2 : bs - 1);
+    compute(kt, st, bs);
+    if (kt + kN >= je) break;                            // workgroup-uniform
+    wait_vmem<3>();
+    lds_barrier();
+    kt += kN;
+    st ^= 1;
+    bs = bs == 2 ? 0 : bs + 1;
+  }
+  // Prefetches past the last tile may be outstanding: drain them before the
+  // wave ends.
+  __builtin_amdgcn_s_waitcnt(0);
 
   if (!wact) return;
   const float lt = l_run + xor_lane(l_run, 32);
@@ -524,9 +517,7 @@ prefill_bf16_kernel(const PrefillParams P) {
 
 }  // namespace
 
-size_t prefill_bf16_lds_bytes(int pid_cap) {
-  return (size_t)kPidOff + (size_t)pid_cap * 4 + (size_t)kPrefillWaves * 4;
-}
+size_t prefill_bf16_lds_bytes(int pid_cap) { return (size_t)kPidOff + (size_t)pid_cap * 4; }
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) {
   // Raise the kernel's dynamic LDS limit once per process (thread-safe).

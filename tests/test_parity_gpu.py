@@ -73,6 +73,10 @@ PREFILL_CASES = [
     ("tp8_global", 15, [1200, 300], [600, 300], 6, 1, 128, 0, 8192, "bf16"),
     ("tp4_local", 16, [700, 40], [700, 40], 12, 4, 128, 512, 512, "bf16"),
     ("tp4_global", 17, [800, 64], [400, 64], 12, 2, 128, 0, 8192, "bf16"),
+    # The smaller model of the family (hidden 4096: 32 query heads of 128;
+    # the KV head counts 16 local / 8 global are a reading, not on the pages).
+    ("small_local", 18, [1100, 300], [1100, 300], 32, 16, 128, 512, 512, "bf16"),
+    ("small_global", 19, [900, 2000], [900, 400], 32, 8, 128, 0, 8192, "bf16"),
 ]
 
 
@@ -214,6 +218,9 @@ DECODE_CASES = [
     ("tp8_global", 46, [5000, 700, 8192], 6, 1, 128, 0, 8192, [1, 8, 0]),
     ("tp4_local", 48, [1500, 513], 12, 4, 128, 512, 512, [1, 0]),
     ("tp4_global", 47, [3000, 4100], 12, 2, 128, 0, 8192, [1, 4, 0]),
+    # The smaller model's shapes (32 query heads; KV heads 16 / 8, a reading).
+    ("small_local", 49, [1500, 513, 17], 32, 16, 128, 512, 512, [1, 2, 0]),
+    ("small_global", 51, [5000, 4096, 33], 32, 8, 128, 0, 8192, [1, 8, 0]),
 ]
 
 
@@ -376,6 +383,30 @@ def test_full_global_decode(splits):
     _say(f"full global_decode splits={splits}")
     ref, _ = oracle.run_batch(b)
     U.compare(U.decode(U.Dev(b), splits=splits), ref, "bf16", f"global_decode/s{splits}")
+
+
+@pytest.mark.parametrize("name,splits", [("small_local_decode", [1, 0]),
+                                         ("small_global_decode", [1, 8, 0])])
+@pytest.mark.timeout(400)
+def test_full_small_decode(name, splits):
+    """The smaller model's decode batches (32 query heads) at full size."""
+    b = _full(name)
+    ref, _ = oracle.run_batch(b)
+    d = U.Dev(b)
+    for s in splits:
+        _say(f"full {name} splits={s}")
+        U.compare(U.decode(d, splits=s), ref, "bf16", f"{name}/s{s}")
+
+
+@pytest.mark.timeout(600)
+def test_full_small_local_prefill_all_rows():
+    """The smaller model's local prefill batch at full size, every row."""
+    b = _full("small_local_prefill")
+    _say("full small_local_prefill (all rows)")
+    out = U.prefill(U.Dev(b))
+    torch.cuda.synchronize()
+    ref, _ = oracle.run_batch(b)
+    U.compare(out, ref, "bf16", "small_local_prefill")
 
 
 @pytest.mark.timeout(400)
