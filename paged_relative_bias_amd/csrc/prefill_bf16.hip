@@ -239,11 +239,15 @@ prefill_bf16_kernel(const PrefillParams P) {
   // K/V of the tile at kt into LDS stage st.  The descriptors of the tile's
   // two pages end at key je (keys past it, and whole tiles past the last,
   // read zero without traffic).  No control flow around any load.
-  auto issue_kv = [&](int kt, int st) {
+  // The tile's two page ids (read from the LDS table ahead of their use).
+  auto page_ids = [&](int kt) {
     const int pi0 = imin((kt >> 4) - pg_lo, P.pid_cap - 1);        // >= 0
     const int pi1 = imin(pi0 + 1, P.pid_cap - 1);
-    const uint64_t page0 = (uint32_t)__builtin_amdgcn_readfirstlane(pid_lds[pi0]);
-    const uint64_t page1 = (uint32_t)__builtin_amdgcn_readfirstlane(pid_lds[pi1]);
+    return make_int2(pid_lds[pi0], pid_lds[pi1]);
+  };
+  auto issue_kv = [&](int kt, int st, int2 pids) {
+    const uint64_t page0 = (uint32_t)__builtin_amdgcn_readfirstlane(pids.x);
+    const uint64_t page1 = (uint32_t)__builtin_amdgcn_readfirstlane(pids.y);
     const int nk = __builtin_amdgcn_readfirstlane(je - kt);
     const uint32_t n0 = sgpr_u32((uint32_t)(nk <= 0 ? 0 : (nk >= 16 ? 16 : nk)) * slot_bytes);
     const uint32_t n1 = sgpr_u32((uint32_t)(nk <= 16 ? 0 : (nk >= 32 ? 16 : nk - 16)) * slot_bytes);
@@ -311,8 +315,17 @@ prefill_bf16_kernel(const PrefillParams P) {
   float l_run = 0.f;
 
   // ---- compute one tile from LDS stage st ----------------------------------
-  auto compute = [&](int kt, int st, int bs) {
-    if (!wave_tile(kt)) return;                           // wave-uniform
+  // `between` issues the loads of later tiles: it runs after this tile's
+  // LDS reads are issued and before their first use, so that its scalar
+  // work overlaps their latency.
+  auto compute = [&](int kt, int st, int bs, auto&& between) {
+    // The next tile's page ids first: their LDS reads complete in order, so
+    // the wait for them in `between` does not wait for this tile's operands.
+    const int2 pids = page_ids(kt + kN);
+    if (!wave_tile(kt)) {                                 // wave-uniform
+      between(pids);
+      return;
+    }
     const bf16* Ks = reinterpret_cast<const bf16*>(smem + (size_t)st * kStage);
     const bf16* Vs = reinterpret_cast<const bf16*>(smem + (size_t)st * kStage + kKBytes);
     const int D0 = pc - kt - 16 * u;                       // distance of element 0
@@ -344,28 +357,34 @@ prefill_bf16_kernel(const PrefillParams P) {
         }
       }
     }
-    // S^T = K . Q^T.  Logical chunk 2 s + u of row col sits at chunk
-    // (2 s + u) ^ (col & 7) = 2 ((s & 3) ^ y) + z + 8 (s >> 2).
-    f32x16 s = f32x16{};
+    // K operands of S^T = K . Q^T.  Logical chunk 2 s + u of row col sits at
+    // chunk (2 s + u) ^ (col & 7) = 2 ((s & 3) ^ y) + z + 8 (s >> 2).
+    bf16x8 kop[8];
     {
       const int y = (col & 7) >> 1, z = u ^ (col & 1);
       const bf16* krow = Ks + col * kD + 64 * (col >> 3) + 8 * z;
 #pragma unroll
       for (int s2 = 0; s2 < 8; ++s2)
-        s = mfma32(*reinterpret_cast<const bf16x8*>(krow + 16 * ((s2 & 3) ^ y) + 64 * (s2 >> 2)),
-                   qop[s2], s);
+        kop[s2] = *reinterpret_cast<const bf16x8*>(krow + 16 * ((s2 & 3) ^ y) + 64 * (s2 >> 2));
     }
+    // The lane's bias run (window tiles): halfword m of its 32 bytes is
+    // entry D0 - 15 + m, i.e. element 15 - m.
+    const bool win = unclamped(kt);                       // wave-uniform
+    uint2 w4[4];
+    if (win) {
+      const bf16* run = reinterpret_cast<const bf16*>(
+          smem + kBiasOff + (uint32_t)(bs * kPrefillWaves + wave) * kBiasWave + b_read);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) __builtin_memcpy(&w4[k], run + 4 * k, 8);
+    }
+    between(pids);
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) s = mfma32(kop[s2], qop[s2], s);
     // Element i (S^T row 8 (i / 4) + 4u + i % 4 = key kt + 16u + i) sits at
     // distance D0 - i.
     float bias[16];
-    if (unclamped(kt)) {                                  // wave-uniform
-      // Halfword m of the lane's 32-byte run is entry D0 - 15 + m, i.e.
-      // element 15 - m.
-      const bf16* run = reinterpret_cast<const bf16*>(
-          smem + kBiasOff + (uint32_t)(bs * kPrefillWaves + wave) * kBiasWave + b_read);
-      uint2 w4[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) __builtin_memcpy(&w4[k], run + 4 * k, 8);
+    if (win) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         bias[15 - 4 * k] = bf16_lo(w4[k].x);
@@ -466,7 +485,7 @@ prefill_bf16_kernel(const PrefillParams P) {
   lds_barrier();                                         // page ids ready
   int kt = jb & ~15;
   int st = 0, bs = 0;
-  issue_kv(kt, 0);
+  issue_kv(kt, 0, page_ids(kt));
   issue_bias(kt, 0);
   issue_bias(kt + kN, 1);
   wait_vmem<3>();
@@ -485,9 +504,10 @@ prefill_bf16_kernel(const PrefillParams P) {
   }
   lds_barrier();
   while (true) {
-    issue_kv(kt + kN, st ^ 1);
-    issue_bias(kt + 2 * kN, bs == 0 ? 2 : bs - 1);
-    compute(kt, st, bs);
+    compute(kt, st, bs, [&](int2 pids) {
+      issue_kv(kt + kN, st ^ 1, pids);
+      issue_bias(kt + 2 * kN, bs == 0 ? 2 : bs - 1);
+    });
     if (kt + kN >= je) break;                            // workgroup-uniform
     wait_vmem<3>();
     lds_barrier();
