@@ -549,8 +549,13 @@ decode_kernel(const DecodeParams P) {
   }
 }
 
-// One wave per (sequence, head) row; lane covers d = lane + 64 * k.  Splits
-// with lse = -inf (empty) are skipped; the order of the sum is fixed.
+// One wave per (sequence, head) row.  The split log-sum-exps are read one
+// per lane (two for more than 64 splits), their max and the weight sum are
+// wave reductions, and each split's weight reaches the whole wave as a
+// scalar, so that empty splits (lse = -inf) skip their row with a uniform
+// branch.  Lane l accumulates d = l + 64 k; the partial rows of up to 8
+// splits are in flight at once.  The order of the sum is fixed (split
+// order), with no atomics.
 template <typename T, int D>
 __global__ void __launch_bounds__(256)
 combine_kernel(const CombineParams P) {
@@ -558,23 +563,41 @@ combine_kernel(const CombineParams P) {
   if (row >= P.rows) return;
   const int lane = threadIdx.x & 63;
   constexpr int PER = D / 64;
-  float M = kNegInf;
-  for (int s = 0; s < P.num_splits; ++s)
-    M = fmaxf(M, P.part_lse[(int64_t)s * P.rows + row]);
+  const int S = P.num_splits;
+  const float l0 = lane < S ? P.part_lse[(int64_t)lane * P.rows + row] : kNegInf;
+  const float l1 = lane + 64 < S ? P.part_lse[(int64_t)(lane + 64) * P.rows + row] : kNegInf;
+  float M = fmaxf(l0, l1);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, xor_lane(M, m));
+  const float w0 = M == kNegInf || l0 == kNegInf ? 0.f : expf(l0 - M);
+  const float w1 = M == kNegInf || l1 == kNegInf ? 0.f : expf(l1 - M);
+  float den = w0 + w1;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) den += xor_lane(den, m);
   float num[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) num[k] = 0.f;
-  float den = 0.f;
-  if (M != kNegInf) {
-    for (int s = 0; s < P.num_splits; ++s) {
-      const float l = P.part_lse[(int64_t)s * P.rows + row];
-      if (l == kNegInf) continue;
-      const float w = expf(l - M);
-      den += w;
-      const float* po = P.part_o + ((int64_t)s * P.rows + row) * D;
+  const float* po = P.part_o + (int64_t)row * D + lane;
+  const int64_t split_stride = (int64_t)P.rows * D;
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float v[8][PER];
+    float w[8];
 #pragma unroll
-      for (int k = 0; k < PER; ++k) num[k] += w * po[lane + 64 * k];
+    for (int j = 0; j < 8; ++j) {
+      const int s = s0 + j;
+      // The split's weight, from lane s % 64 of w0 (s < 64) or w1.
+      const float wl = s < 64 ? w0 : w1;
+      w[j] = s < S ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                   __builtin_bit_cast(int, wl), s & 63))
+                   : 0.f;
+#pragma unroll
+      for (int k = 0; k < PER; ++k)
+        v[j][k] = w[j] != 0.f ? po[s * split_stride + 64 * k] : 0.f;   // uniform branch
     }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int k = 0; k < PER; ++k) num[k] += w[j] * v[j][k];
   }
   T* dst = static_cast<T*>(P.out) + (int64_t)row * D;
 #pragma unroll
