@@ -52,6 +52,9 @@ FP32_PEAK_TFLOPS = 157.3
 MALL_BYTES = 256 << 20
 DECODE_KERNEL_SRC = os.path.join(ROOT, "paged_relative_bias_amd", "csrc", "decode.hip")
 PREFILL_KERNEL_SRC = os.path.join(ROOT, "paged_relative_bias_amd", "csrc", "prefill.hip")
+# bf16 with head_dim 128 and no append (every bench workload without --append).
+PREFILL_BF16_KERNEL_SRC = os.path.join(ROOT, "paged_relative_bias_amd", "csrc", "prefill_bf16.hip")
+DEVICE_HELPERS_SRC = os.path.join(ROOT, "paged_relative_bias_amd", "csrc", "device.hpp")
 PROFILES = os.path.join(ROOT, "profiles")
 HEADLINE = "local_decode"
 # The other records: generator -> [(record name, decode split count (0 =
@@ -209,7 +212,7 @@ class Workload:
         self.replicas = replicas or max(2, math.ceil(2 * MALL_BYTES / self.step_bytes) + 1)
         self.stream = torch.cuda.current_stream()
         self.launch_stream = torch.cuda.Stream() if graph else self.stream
-        self.kernel_srcs = set()
+        self.kernel_srcs = {DEVICE_HELPERS_SRC}
         self.splits_used = []
         calls, self.keep = [], []
         for r in range(self.replicas):
@@ -261,7 +264,8 @@ class Workload:
                     rc.append(("inkling_rel_attn_prefill_append" if append
                                else "inkling_rel_attn_prefill", a))
                     self.keep += [q, k, v, rel, bt, sl, cu, out, dims]
-                    self.kernel_srcs.add(PREFILL_KERNEL_SRC)
+                    fast = p.dtype == "bf16" and p.head_dim == 128 and not append
+                    self.kernel_srcs.add(PREFILL_BF16_KERNEL_SRC if fast else PREFILL_KERNEL_SRC)
             calls.append(rc)
         torch.cuda.synchronize()
         lib = binding.load()
