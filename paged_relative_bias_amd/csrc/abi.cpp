@@ -223,9 +223,9 @@ inkling_status_t prefill_impl(const void* q, const void* k_new, const void* v_ne
   // Pages a workgroup's key range can touch.
   const int64_t span = window > 0 ? (int64_t)p.bq + window - 1 : (int64_t)dims->max_seq_len;
   p.pid_cap = (int32_t)std::min<int64_t>(dims->max_blocks_per_seq, (span + 15) / 16 + 2);
-  // bf16 with head_dim 128 and no append runs the specialised kernel.
-  const bool bf16_fast = dims->dtype == INKLING_DTYPE_BF16 && dims->head_dim == 128 &&
-                         k_new == nullptr;
+  // bf16 with head_dim 128 runs the specialised kernel (with or without the
+  // fused append).
+  const bool bf16_fast = dims->dtype == INKLING_DTYPE_BF16 && dims->head_dim == 128;
   if ((bf16_fast ? prefill_bf16_lds_bytes(p.pid_cap)
                  : prefill_lds_bytes(dims->dtype, dims->head_dim, waves, p.sb_pitch, p.pid_cap)) >
       160 * 1024)

@@ -93,6 +93,11 @@ __device__ __forceinline__ void lds_barrier() {
 // fp32 value of the bf16 held in bits [15:0] of w.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 
+// APPEND: the new tokens' K/V rows (keys pbase .. je - 1) come from
+// P.k_new / P.v_new, never from the cache, and each workgroup stores its own
+// tokens' rows into the cache, so no workgroup waits for another's store (a
+// separate instantiation: the plain kernel's loads stay free of it).
+template <bool APPEND>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_bf16_kernel(const PrefillParams P) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -173,6 +178,8 @@ prefill_bf16_kernel(const PrefillParams P) {
   const uint32_t head_bytes = (uint32_t)g * kD * SZ;
   const char* kg = static_cast<const char*>(P.k);
   const char* vg = static_cast<const char*>(P.v);
+  const uint64_t kn = reinterpret_cast<uint64_t>(P.k_new);
+  const uint64_t vn = reinterpret_cast<uint64_t>(P.v_new);
   // K/V loads.  Wave w's load i writes LDS rows 4 (2w + i) .. + 3 (one 1 KB
   // block, lane l at bytes 16 l .. 16 l + 15 after M0), which hold keys
   // 16 i + 4 w + l / 16: slot 4 w + l / 16 of page i of the tile.  Lane l
@@ -251,14 +258,31 @@ prefill_bf16_kernel(const PrefillParams P) {
     const int nk = __builtin_amdgcn_readfirstlane(je - kt);
     const uint32_t n0 = sgpr_u32((uint32_t)(nk <= 0 ? 0 : (nk >= 16 ? 16 : nk)) * slot_bytes);
     const uint32_t n1 = sgpr_u32((uint32_t)(nk <= 16 ? 0 : (nk >= 32 ? 16 : nk - 16)) * slot_bytes);
-    const __amdgpu_buffer_rsrc_t rk0 =
-        make_rsrc(reinterpret_cast<const void*>(sgpr_u64(reinterpret_cast<uint64_t>(kg) + page0 * page_bytes)), n0);
-    const __amdgpu_buffer_rsrc_t rk1 =
-        make_rsrc(reinterpret_cast<const void*>(sgpr_u64(reinterpret_cast<uint64_t>(kg) + page1 * page_bytes)), n1);
-    const __amdgpu_buffer_rsrc_t rv0 =
-        make_rsrc(reinterpret_cast<const void*>(sgpr_u64(reinterpret_cast<uint64_t>(vg) + page0 * page_bytes)), n0);
-    const __amdgpu_buffer_rsrc_t rv1 =
-        make_rsrc(reinterpret_cast<const void*>(sgpr_u64(reinterpret_cast<uint64_t>(vg) + page1 * page_bytes)), n1);
+    uint64_t kb0 = reinterpret_cast<uint64_t>(kg) + page0 * page_bytes;
+    uint64_t kb1 = reinterpret_cast<uint64_t>(kg) + page1 * page_bytes;
+    uint64_t vb0 = reinterpret_cast<uint64_t>(vg) + page0 * page_bytes;
+    uint64_t vb1 = reinterpret_cast<uint64_t>(vg) + page1 * page_bytes;
+    if constexpr (APPEND) {
+      // A page whose keys are all new reads the new rows instead: slot s is
+      // new token (page's first key + s - pbase), so the rows are addressed
+      // like a page whose base sits that many rows after k_new's token q0.
+      // (A page that straddles pbase reads the cache and is patched once it
+      // has landed.)
+      if (kt >= pbase) {                                 // wave-uniform
+        const uint64_t off = (uint64_t)(q0 + kt - pbase) * slot_bytes;
+        kb0 = kn + off;
+        vb0 = vn + off;
+      }
+      if (kt + 16 >= pbase) {
+        const uint64_t off = (uint64_t)(q0 + kt + 16 - pbase) * slot_bytes;
+        kb1 = kn + off;
+        vb1 = vn + off;
+      }
+    }
+    const __amdgpu_buffer_rsrc_t rk0 = make_rsrc(reinterpret_cast<const void*>(sgpr_u64(kb0)), n0);
+    const __amdgpu_buffer_rsrc_t rk1 = make_rsrc(reinterpret_cast<const void*>(sgpr_u64(kb1)), n1);
+    const __amdgpu_buffer_rsrc_t rv0 = make_rsrc(reinterpret_cast<const void*>(sgpr_u64(vb0)), n0);
+    const __amdgpu_buffer_rsrc_t rv1 = make_rsrc(reinterpret_cast<const void*>(sgpr_u64(vb1)), n1);
     // Block kb = 2 w + i: K at kb * 1024 + 128 * (kb >> 1), V at kKBytes +
     // kb * 1024.  The compiler does not see these loads; every wait for them
     // is explicit, and nothing else in the kernel uses M0.
@@ -471,6 +495,27 @@ prefill_bf16_kernel(const PrefillParams P) {
       for (int ks = 0; ks < 2; ++ks) acc[dt] = mfma32(va[dt][ks], pl[ks], acc[dt]);
   };
 
+  // Append: the tile at kt in stage st straddles the first new token
+  // (pbase inside it, so one of its pages was read from the cache).  Each
+  // wave replaces its own rows of new keys with the new rows, after its own
+  // loads of the tile completed and before the barrier that publishes them.
+  auto patch_new = [&](int kt, int st) {
+    if (!(kt < pbase && kt + kN > pbase)) return;        // workgroup-uniform
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int key = kt + 16 * i + 4 * wave + (lane >> 4);
+      if (key >= pbase && key < je) {
+        // Row q0 + key - pbase; k_lane / v_lane hold the slot term of key.
+        const int64_t shift = (int64_t)(q0 + kt + 16 * i - pbase) * slot_bytes;
+        const uint4 a = *reinterpret_cast<const uint4*>(kn + (uint64_t)((int64_t)k_lane[i] + shift));
+        const uint4 c = *reinterpret_cast<const uint4*>(vn + (uint64_t)((int64_t)v_lane + shift));
+        const uint32_t blk = (uint32_t)st * kStage + (uint32_t)(2 * wave + i) * 1024u + 16u * (uint32_t)lane;
+        *reinterpret_cast<uint4*>(smem + blk + 128u * (uint32_t)wave) = a;
+        *reinterpret_cast<uint4*>(smem + blk + kKBytes) = c;
+      }
+    }
+  };
+
   // ---- software pipeline over key tiles ------------------------------------
   // At the top of each step tile kt sits in K/V stage st and bias stage bs,
   // the next tile's bias is in flight into the stage after; tile kt + N's
@@ -483,12 +528,33 @@ prefill_bf16_kernel(const PrefillParams P) {
   // so no load sits under control flow.  Nothing the compiler sees is loaded
   // in the loop outside the rare clamp path, so it adds no waits of its own.
   lds_barrier();                                         // page ids ready
+  if constexpr (APPEND) {
+    // Store this workgroup's tokens' new K/V rows of head g into the cache
+    // (16 chunks of 16 bytes per row and tensor).  With valid metadata every
+    // new key's page is in the table; a clipped table only follows from
+    // lengths above max_seq_len, whose result is unspecified: skip those.
+    const int chunks = (tend - t0) * 32;
+    for (int c = tid; c < chunks; c += blockDim.x) {
+      const int t = t0 + (c >> 5), r = c & 31;
+      const bool isv = r >= 16;
+      const int key = pbase + t;
+      const int pi = (key >> 4) - pg_lo;
+      if (pi >= npg) continue;
+      const uint64_t page = (uint32_t)pid_lds[pi];
+      const uint64_t dst = page * page_bytes + (uint64_t)(key & 15) * slot_bytes + head_bytes +
+                           (uint64_t)(r & 15) * 16u;
+      const uint64_t src = (uint64_t)(q0 + t) * slot_bytes + head_bytes + (uint64_t)(r & 15) * 16u;
+      const uint4 v = *reinterpret_cast<const uint4*>((isv ? vn : kn) + src);
+      *reinterpret_cast<uint4*>(reinterpret_cast<char*>(const_cast<void*>(isv ? P.v : P.k)) + dst) = v;
+    }
+  }
   int kt = jb & ~15;
   int st = 0, bs = 0;
   issue_kv(kt, 0, page_ids(kt));
   issue_bias(kt, 0);
   issue_bias(kt + kN, 1);
   wait_vmem<3>();
+  if constexpr (APPEND) patch_new(kt, 0);
   if (kt < jb) {                                         // workgroup-uniform
     // The first page holds keys before the block's first visible key: their
     // P is 0 for every column, but a non-finite V row would still turn 0 * V
@@ -510,6 +576,7 @@ prefill_bf16_kernel(const PrefillParams P) {
     });
     if (kt + kN >= je) break;                            // workgroup-uniform
     wait_vmem<3>();
+    if constexpr (APPEND) patch_new(kt + kN, st ^ 1);
     lds_barrier();
     kt += kN;
     st ^= 1;
@@ -544,14 +611,21 @@ hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) {
   static std::once_flag once;
   static hipError_t attr = hipSuccess;
   std::call_once(once, [] {
-    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_bf16_kernel),
+    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_bf16_kernel<false>),
                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (attr == hipSuccess)
+      attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_bf16_kernel<true>),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   });
   if (attr != hipSuccess) return attr;
   const int64_t total = (int64_t)p.nqb * p.num_seqs * p.hkv;
   const int64_t grid = ((total + 7) / 8) * 8;
-  prefill_bf16_kernel<<<dim3((unsigned)grid), dim3(kPrefillWaves * 64),
-                        prefill_bf16_lds_bytes(p.pid_cap), stream>>>(p);
+  if (p.k_new != nullptr)
+    prefill_bf16_kernel<true><<<dim3((unsigned)grid), dim3(kPrefillWaves * 64),
+                                prefill_bf16_lds_bytes(p.pid_cap), stream>>>(p);
+  else
+    prefill_bf16_kernel<false><<<dim3((unsigned)grid), dim3(kPrefillWaves * 64),
+                                 prefill_bf16_lds_bytes(p.pid_cap), stream>>>(p);
   return hipGetLastError();
 }
 
