@@ -45,6 +45,10 @@
 //     the LDS destination) in the bank-conflict-free layout of the generic
 //     kernel: K row r at byte r * 256 + 128 * (r >> 3), 16-byte chunk c at
 //     c ^ (r & 7); V row r at byte r * 256, chunk c at c ^ (4 * (r & 3)).
+//   * Fused append (a separate instance): pages whose keys are all new are
+//     loaded from the new rows, the one page that straddles the first new
+//     token is patched in LDS, and each workgroup stores its own tokens'
+//     rows into the cache.
 #include <mutex>
 
 #include "device.hpp"
