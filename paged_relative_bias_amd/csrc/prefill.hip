@@ -22,10 +22,9 @@
 //     loads 8 keys of the tile (one page) through a buffer descriptor that
 //     ends at the block's last key (later keys, and tiles past the last,
 //     read zero without traffic); the page ids of the block's range sit in
-//     an LDS table.  bf16 with head_dim 128 (no append) loads them straight
-//     into LDS in a bank-conflict-free layout (rows of D elements with
-//     XOR-swizzled 16-byte chunks, see DMA below); the other forms go
-//     through registers into rows with a 16-byte (K) or 32-byte (V) pad;
+//     an LDS table; they go through registers into rows with a 16-byte (K)
+//     or 32-byte (V) pad (bf16 with head_dim 128 runs the specialised
+//     kernel of prefill_bf16.hip instead);
 //   * every wave copies the bias runs of its 32 rows for the tile: for
 //     (token, head) the tile needs one contiguous run of the distance axis,
 //     taken from an aligned window of sb entries with 16-byte loads;
@@ -113,15 +112,6 @@ prefill_kernel(const PrefillParams P) {
   constexpr int N = C::N, VEC = C::VEC, CPR = C::CPR, KP = C::KP, VP = C::VP, KPI = C::KPI;
   constexpr uint32_t SZ = sizeof(T);
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  // bf16, head_dim 128, no append: K and V rows go from HBM straight into
-  // LDS (16-byte buffer loads with the LDS destination) in rows of D
-  // elements, laid out so that the MFMA operand reads hit distinct banks:
-  //   K row r at byte r * 256 + 128 * (r >> 3), chunk c at c ^ (r & 7)
-  //     (16 lanes reading rows r .. r + 15 at one logical chunk cover all
-  //     64 banks; groups of 8 rows are 128 bytes apart, 8576 bytes in all);
-  //   V row r at byte r * 256, chunk c at c ^ (4 * (r & 3)) (a transposed
-  //     read's four rows then use 16 different chunks).
-  constexpr bool DMA = C::kBF16 && D == 128 && !APPEND;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -230,16 +220,10 @@ prefill_kernel(const PrefillParams P) {
   // multiples of 16); its load i of K (and of V) covers keys KW*w + KPI*i +
   // lane / CPR, 16-byte chunk lane % CPR.
   uint32_t kv_lane[C::LPT];
-  uint32_t v_lane[C::LPT];       // V offsets (the DMA layout swizzles V differently)
 #pragma unroll
   for (int i = 0; i < C::LPT; ++i) {
     const int row = C::KW * wave + KPI * i + lane / CPR;
-    // Lane l writes physical chunk l % CPR of its row, so it fetches the
-    // logical chunk that the layout puts there.
-    const int chk = DMA ? ((lane % CPR) ^ (row & 7)) : (lane % CPR);
-    const int chv = DMA ? ((lane % CPR) ^ (4 * (row & 3))) : (lane % CPR);
-    kv_lane[i] = (uint32_t)(row & 15) * slot_bytes + head_bytes + (uint32_t)chk * 16u;
-    v_lane[i] = (uint32_t)(row & 15) * slot_bytes + head_bytes + (uint32_t)chv * 16u;
+    kv_lane[i] = (uint32_t)(row & 15) * slot_bytes + head_bytes + (uint32_t)(lane % CPR) * 16u;
   }
   // Bias load i: row r = c / sbc (token rt, head rh), chunk c % sbc.
   uint32_t b_row[C::BIAS_PER];   // row offset | 0x80000000 if the row is unused
@@ -283,36 +267,10 @@ prefill_kernel(const PrefillParams P) {
           sgpr_u64(all_new ? vn + new_off : reinterpret_cast<uint64_t>(vg) + page * page_bytes);
       const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const void*>(kb), nrec);
       const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const void*>(vb), nrec);
-      if constexpr (DMA) {
-        // Rows KW * wave + KPI * i .. + KPI - 1 of the stage: one 1 KB block
-        // per load (lane l writes bytes 16 l .. 16 l + 15 after M0).  Lanes
-        // out of the descriptor's range write zeros.  The compiler does not
-        // see these loads: the bias loads issued after them in issue() are
-        // waited for before commit(), which (loads completing in order)
-        // also completes these, and nothing else in the kernel uses M0.
-        // Rows of load i: 4-row block kb = KW * wave / KPI + i, K at byte
-        // kb * 1024 + 128 * (kb >> 1), V at kb * 1024.
-        const uint32_t sl = sgpr_u32((uint32_t)(st_to * C::stage_bytes()));
-        const int kb0 = C::KW * wave / KPI;                // wave-uniform
 #pragma unroll
-        for (int i = 0; i < C::LPT; ++i) {
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-          const int kb = kb0 + i;
-          const uint32_t klds = sgpr_u32(sl + (uint32_t)kb * 1024u + 128u * (uint32_t)(kb >> 1));
-          const uint32_t vlds = sgpr_u32(sl + (uint32_t)(N * KP) * SZ + (uint32_t)kb * 1024u);
-          asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                       :: "s"(klds), "v"(kv_lane[i]), "s"(rk) : "memory", "m0");
-          asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                       :: "s"(vlds), "v"(v_lane[i]), "s"(rv) : "memory", "m0");
-#pragma clang diagnostic pop
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < C::LPT; ++i) {
-          rg.kv[i] = bload128(rk, kv_lane[i]);
-          rg.kv[C::LPT + i] = bload128(rv, kv_lane[i]);
-        }
+      for (int i = 0; i < C::LPT; ++i) {
+        rg.kv[i] = bload128(rk, kv_lane[i]);
+        rg.kv[C::LPT + i] = bload128(rv, kv_lane[i]);
       }
 
     }
@@ -331,14 +289,12 @@ prefill_kernel(const PrefillParams P) {
   auto commit = [&](const Regs& rg, int st, int kt) {
     T* Ks = stage(st);
     T* Vs = Ks + N * KP;
-    if constexpr (!DMA) {
 #pragma unroll
-      for (int i = 0; i < C::LPT; ++i) {
-        const int key = C::KW * wave + KPI * i + lane / CPR;
-        const int chunk = (lane % CPR) * VEC;
-        *reinterpret_cast<uint4*>(Ks + key * KP + chunk) = rg.kv[i];
-        *reinterpret_cast<uint4*>(Vs + key * VP + chunk) = rg.kv[C::LPT + i];
-      }
+    for (int i = 0; i < C::LPT; ++i) {
+      const int key = C::KW * wave + KPI * i + lane / CPR;
+      const int chunk = (lane % CPR) * VEC;
+      *reinterpret_cast<uint4*>(Ks + key * KP + chunk) = rg.kv[i];
+      *reinterpret_cast<uint4*>(Vs + key * VP + chunk) = rg.kv[C::LPT + i];
     }
     if constexpr (APPEND) {
       const int key0 = kt + C::KW * wave;                 // wave-uniform
@@ -431,23 +387,15 @@ prefill_kernel(const PrefillParams P) {
         // before the first PV MFMA, as both P terms use them.
         const int jj = lane & 15;
         const int dgrp = (lane >> 4) & 1;
-        // DMA layout: element e of row r sits at chunk (e / 8) ^ (4 (r & 3));
-        // the rows 4 u + jj / 4 (+ 8, + 16) share r & 3 = jj / 4, so d-block
-        // dt of the lane's columns starts 32 (dt ^ (jj / 4)) elements into the
-        // row: one base per dt plus immediate row offsets.
-        const T* vbase = Vs + (4 * u + (jj >> 2)) * D + 8 * (2 * dgrp + ((jj & 3) >> 1)) +
-                         4 * (jj & 1);
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
-          const T* vb = DMA ? vbase + 32 * (dt ^ (jj >> 2))
-                            : Vs + (4 * u + (jj >> 2)) * VP + 32 * dt + 16 * dgrp + 4 * (jj & 3);
-          constexpr int VPd = DMA ? D : VP;
+          const T* vb = Vs + (4 * u + (jj >> 2)) * VP + 32 * dt + 16 * dgrp + 4 * (jj & 3);
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
             const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) i16x4*)(vb + (16 * ks) * VPd));
+                (__attribute__((address_space(3))) i16x4*)(vb + (16 * ks) * VP));
             const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) i16x4*)(vb + (16 * ks + 8) * VPd));
+                (__attribute__((address_space(3))) i16x4*)(vb + (16 * ks + 8) * VP));
             const i16x8 a16 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             va[dt][ks] = __builtin_bit_cast(bf16x8, a16);
           }
@@ -457,21 +405,10 @@ prefill_kernel(const PrefillParams P) {
     if constexpr (C::kBF16 && !APPEND) read_vt();
     f32x16 s = f32x16{};
     if constexpr (C::kBF16) {
-      if constexpr (DMA) {
-        // Logical chunk 2 st2 + u of row col sits at chunk (2 st2 + u) ^
-        // (col & 7) = 2 ((st2 & 3) ^ y) + z + 8 (st2 >> 2).
-        const int y = (col & 7) >> 1, z = u ^ (col & 1);
-        const bf16* krow = Ks + col * D + 64 * (col >> 3) + 8 * z;
+      const bf16* krow = Ks + col * KP + 8 * u;
 #pragma unroll
-        for (int st2 = 0; st2 < C::QSTEPS; ++st2)
-          s = mfma32(*reinterpret_cast<const bf16x8*>(krow + 16 * ((st2 & 3) ^ y) + 64 * (st2 >> 2)),
-                     qop[st2], s);
-      } else {
-        const bf16* krow = Ks + col * KP + 8 * u;
-#pragma unroll
-        for (int st2 = 0; st2 < C::QSTEPS; ++st2)
-          s = mfma32(*reinterpret_cast<const bf16x8*>(krow + 16 * st2), qop[st2], s);
-      }
+      for (int st2 = 0; st2 < C::QSTEPS; ++st2)
+        s = mfma32(*reinterpret_cast<const bf16x8*>(krow + 16 * st2), qop[st2], s);
     } else {
       const float* krow = Ks + col * KP + u;
 #pragma unroll
@@ -644,9 +581,8 @@ prefill_kernel(const PrefillParams P) {
     __builtin_amdgcn_s_waitcnt(0);
     lds_barrier();
     T* Vs = stage(0) + N * KP;
-    constexpr int VROW = DMA ? D : VP;                     // V row pitch (elements)
     for (int c = tid; c < (jb - kt) * CPR; c += blockDim.x)
-      *reinterpret_cast<uint4*>(Vs + (c / CPR) * VROW + (c % CPR) * VEC) = make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4*>(Vs + (c / CPR) * VP + (c % CPR) * VEC) = make_uint4(0u, 0u, 0u, 0u);
   }
   lds_barrier();
   while (true) {
@@ -719,8 +655,8 @@ size_t prefill_lds_bytes(int dtype, int head_dim, int waves, int sb_pitch, int p
 }
 
 hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim, hipStream_t stream) {
-  if (dtype == 0)
-    return head_dim == 64 ? launch_t<bf16, 64>(p, stream) : launch_t<bf16, 128>(p, stream);
+  // bf16 with head_dim 128 runs prefill_bf16_kernel (launch_prefill_bf16).
+  if (dtype == 0) return head_dim == 64 ? launch_t<bf16, 64>(p, stream) : hipErrorInvalidValue;
   return head_dim == 64 ? launch_t<float, 64>(p, stream) : launch_t<float, 128>(p, stream);
 }
 
