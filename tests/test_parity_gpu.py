@@ -481,3 +481,44 @@ def test_full_global_mixed_all_rows():
     U.compare(o_dec, ref_dec, "bf16", "global_mixed/decode")
     ref_pre, _ = oracle.run_batch(pre)
     U.compare(o_pre, ref_pre, "bf16", "global_mixed/chunks")
+
+
+@pytest.mark.timeout(300)
+def test_pool_above_4gib():
+    """Page pools of 70000 pages of 64 KB (4.6 GB each for K and V), with the
+    batch's pages moved to physical ids from 65600 on, so that every page's
+    byte offset into the pool exceeds 2^32: prefill and split-KV decode read
+    the same keys as from the small pool.  The rest of the pool is never
+    written (uninitialised device memory) and must never be read."""
+    big_pages, base = 70_000, 65_600
+    for kind, L, n, W in (("prefill", [700, 300, 33], [700, 300, 33], 512),
+                          ("decode", [2000, 1500, 513, 16], [1, 1, 1, 1], 0)):
+        b = _mk(90, L, n, Hq=48, Hkv=16, D=128, W=W)
+        assert base + b.num_blocks <= big_pages
+        shape = (big_pages,) + tuple(b.k_cache.shape[1:])
+        assert big_pages * b.k_cache[0].numel() * 2 > (1 << 32)
+        _say(f"pool above 4 GiB: {kind} L={L} pages {base}..{base + b.num_blocks - 1}")
+        k = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+        v = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+        k[base:base + b.num_blocks] = b.k_cache.cuda()
+        v[base:base + b.num_blocks] = b.v_cache.cuda()
+        bt = torch.from_numpy(np.where(b.block_table >= 0, b.block_table + base, -1).astype(np.int32)).cuda()
+        q, rel = b.q.cuda(), b.rel_logits.cuda()
+        sl = torch.from_numpy(b.seq_lens).cuda()
+        ref, _ = oracle.run_batch(b)
+        if kind == "prefill":
+            cu = torch.from_numpy(b.cu_q_lens).cuda()
+            out = torch.full_like(q, float("nan"))
+            binding.prefill(q, k, v, bt, sl, cu, rel, b.window, b.scale, out,
+                            max_q_len=b.max_q_len, max_seq_len=b.max_seq_len)
+            torch.cuda.synchronize()
+            U.compare(out, ref, "bf16", "pool_above_4gib/prefill")
+        else:
+            for s in (1, 4):
+                out = torch.full_like(q, float("nan"))
+                binding.decode(q, k, v, bt, sl, rel, b.window, b.scale, out,
+                               max_seq_len=b.max_seq_len, num_splits=s)
+                torch.cuda.synchronize()
+                U.compare(out, ref, "bf16", f"pool_above_4gib/decode/s{s}")
+        del k, v
+        torch.cuda.empty_cache()
