@@ -19,9 +19,10 @@ split, long-context global decode, and the smaller model's shapes).
 
 Timing: W untimed warm-up steps, then exactly K steps bracketed by
 torch.cuda.synchronize(); two HIP events on the launch stream around the
-timed region give the back-to-back mean, and a separate pass with an event
-pair around every step (at least 50) gives the median and p10/p90 launch
-durations.  The roofline fractions use the median.  Consecutive steps read
+timed region give the back-to-back mean launch time, from which the
+roofline fractions are computed, and a separate pass with an event pair
+around every step (at least 50) gives the median and p10/p90 launch
+durations, reported beside it.  Consecutive steps read
 different device copies of the inputs (replicas rotated round-robin, at
 least 512 MB apart) so no step finds its data in the 256 MB Infinity Cache
 left behind by the previous one, as in a real forward where consecutive
