@@ -14,8 +14,9 @@ local-layer decode batch (64 sequences, contexts U[1024, 8192], 48 query /
 16 KV heads, head_dim 128, window 512, bf16).  Without --workload the line
 also carries `workloads`: one record of the same fields for every other
 serving configuration (global decode at the library's split count and at 1,
-8 and 32 splits, local prefill, the global mixed batch as one call and
-split, long-context global decode, and the smaller model's shapes).
+8 and 32 splits, and replayed from a HIP graph; local prefill; the global
+mixed batch as one call and split; long-context global decode; and the
+smaller model's shapes).
 
 Timing: W untimed warm-up steps, then exactly K steps bracketed by
 torch.cuda.synchronize(); two HIP events on the launch stream around the
@@ -59,10 +60,12 @@ DEVICE_HELPERS_SRC = os.path.join(ROOT, "paged_relative_bias_amd", "csrc", "devi
 PROFILES = os.path.join(ROOT, "profiles")
 HEADLINE = "local_decode"
 # The other records: generator -> [(record name, decode split count (0 =
-# the library's choice))]; each generated batch serves all of its records.
+# the library's choice)[, launched as HIP graph replays])]; each generated
+# batch serves all of its records.
 SECONDARY = [
     ("global_decode", [("global_decode", 0), ("global_decode_s1", 1),
-                       ("global_decode_s8", 8), ("global_decode_s32", 32)]),
+                       ("global_decode_s8", 8), ("global_decode_s32", 32),
+                       ("global_decode_graph", 0, True)]),
     ("local_prefill", [("local_prefill", 0)]),
     ("global_mixed", [("global_mixed", 0), ("global_mixed_split", 0)]),
     ("long_global_decode", [("long_global_decode", 0)]),
@@ -335,7 +338,8 @@ def record_for(name, batch, wl, t, record_name, cpu):
     achieved = wl.step_bytes / (mean * 1e-3) / 1e9
     tflops = wl.step_flops / (mean * 1e-3) / 1e12
     peak_tf = BF16_PEAK_TFLOPS if batch.dtype == "bf16" else FP32_PEAK_TFLOPS
-    traffic = traffic_from_profiles(record_name, sorted(wl.kernel_srcs))
+    # A graph-replayed record runs the same kernels as its eager form.
+    traffic = traffic_from_profiles(record_name.removesuffix("_graph"), sorted(wl.kernel_srcs))
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
@@ -378,17 +382,19 @@ def make_batch_for(gen_name, args, seed):
     return batch
 
 
-def run_record(record_name, batch, splits, args, dev, steps, warmup, cpu):
-    """Time one record on an already generated batch."""
+def run_record(record_name, batch, splits, args, dev, steps, warmup, cpu, graph=None):
+    """Time one record on an already generated batch (graph: replay HIP graphs
+    of the step; None follows --graph)."""
     import torch
 
+    graph = args.graph if graph is None else graph
     kind = "global_mixed_split" if record_name == "global_mixed_split" else batch.name
-    wl = Workload(kind, batch, splits=splits, append=args.append, graph=args.graph,
+    wl = Workload(kind, batch, splits=splits, append=args.append, graph=graph,
                   replicas=args.replicas, dev=dev)
     t = wl.time(steps, warmup)
     rec = record_for(kind, batch, wl, t, record_name, cpu)
     rec["config"]["seed"] = args.seed
-    rec["config"]["launch"] = "hip_graph" if args.graph else "eager"
+    rec["config"]["launch"] = "hip_graph" if graph else "eager"
     rec["config"]["append"] = bool(args.append)
     rec["config"]["bias_spike"] = bool(args.spike)
     r = rec["roofline"]
@@ -511,13 +517,14 @@ def main():
             try:
                 b = make_batch_for(gname, args, args.seed)
                 cpu = baseline(b, args, min(args.cpu_budget, 10.0))
-                for rname, splits in recs:
+                for rname, splits, *graph in recs:
                     others[rname] = run_record(rname, b, splits, args, dev,
-                                               min(args.steps, 100), args.warmup, cpu)
+                                               min(args.steps, 100), args.warmup, cpu,
+                                               graph=graph[0] if graph else None)
                 del b
             except Exception as e:  # keep the headline and the other records
                 log(f"{gname}: failed: {e!r}")
-                for rname, _ in recs:
+                for rname, *_ in recs:
                     others.setdefault(rname, {"error": repr(e)})
             gc.collect()
         line["workloads"] = others
