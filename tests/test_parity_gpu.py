@@ -522,3 +522,35 @@ def test_pool_above_4gib():
                 U.compare(out, ref, "bf16", f"pool_above_4gib/decode/s{s}")
         del k, v
         torch.cuda.empty_cache()
+
+
+def test_shared_prefix_pages():
+    """Prefix caching: sequences whose block tables point at the same physical
+    pages for a common prefix (parallel samples of one prompt).  The shared
+    pages are read by several workgroups of one launch; the oracle reads the
+    same pages through the same table."""
+    # Prefill chunks on top of a shared 512-key prefix (32 pages).
+    b = _mk(70, [900, 700, 612], [100, 60, 100], Hq=48, Hkv=8, D=128, W=0)
+    bt = b.block_table.copy()
+    bt[1, :32] = bt[0, :32]
+    bt[2, :32] = bt[0, :32]
+    b = dataclasses.replace(b, block_table=bt)
+    _say("shared prefix: prefill chunks on a shared 512-key prefix")
+    ref, _ = oracle.run_batch(b)
+    U.compare(U.prefill(U.Dev(b)), ref, "bf16", "shared_prefix/prefill")
+    # Decode rows (local and global layers) sharing a 1024-key prefix (64 pages).
+    # A shared page may hold keys that its first owner's queries no longer see
+    # but another sequence's do, so no key is poisoned as stale here.
+    for W, Hkv in ((512, 16), (0, 8)):
+        b = inputs.make_batch(np.random.default_rng(71 + W), [1100, 1030, 1500, 1040, 1200, 1025],
+                              [1] * 6, num_q_heads=48, num_kv_heads=Hkv, head_dim=128, window=W,
+                              rel_len=W if W > 0 else 8192, poison_stale=False)
+        bt = b.block_table.copy()
+        for i in range(1, 6):
+            bt[i, :64] = bt[0, :64]
+        b = dataclasses.replace(b, block_table=bt)
+        ref, _ = oracle.run_batch(b)
+        d = U.Dev(b)
+        for s in (1, 4):
+            _say(f"shared prefix: decode W={W} splits={s}")
+            U.compare(U.decode(d, splits=s), ref, "bf16", f"shared_prefix/decode/W{W}/s{s}")
