@@ -554,3 +554,25 @@ def test_shared_prefix_pages():
         for s in (1, 4):
             _say(f"shared prefix: decode W={W} splits={s}")
             U.compare(U.decode(d, splits=s), ref, "bf16", f"shared_prefix/decode/W{W}/s{s}")
+
+
+def test_block_table_padding_is_never_read():
+    """Entries past a sequence's ceil(L / 16) pages may hold anything (the
+    header's precondition covers only the first ones): ids far out of range
+    and negative ids there change nothing."""
+    for kind, L, n, W in (("prefill", [300, 47, 700], [300, 47, 100], 0),
+                          ("decode", [300, 47, 700], [1, 1, 1], 512)):
+        b = _mk(80, L, n, Hq=12, Hkv=4, D=128, W=W, max_blocks=64)
+        ref, _ = oracle.run_batch(b)
+        bt = b.block_table.copy()
+        pad = bt < 0
+        assert pad.any()
+        bt[pad] = np.where(np.arange(pad.sum()) % 2 == 0, 0x7fffffff, -7)
+        b2 = dataclasses.replace(b, block_table=bt)
+        _say(f"block-table padding: {kind}")
+        d = U.Dev(b2)
+        if kind == "prefill":
+            U.compare(U.prefill(d), ref, "bf16", "padding/prefill")
+        else:
+            for s in (1, 3):
+                U.compare(U.decode(d, splits=s), ref, "bf16", f"padding/decode/s{s}")
