@@ -576,3 +576,22 @@ def test_block_table_padding_is_never_read():
         else:
             for s in (1, 3):
                 U.compare(U.decode(d, splits=s), ref, "bf16", f"padding/decode/s{s}")
+
+
+def test_many_short_sequences():
+    """Hundreds of short sequences in one call: a grid of mostly one-block
+    sequences whose size is not a multiple of the 8 XCDs, with lengths that
+    end anywhere in a page."""
+    rng = np.random.default_rng(90)
+    L = rng.integers(1, 41, size=301)
+    _say("many short sequences: prefill, 301 sequences of 1-40 tokens")
+    b = _mk(91, L, L, Hq=48, Hkv=16, D=128, W=512)
+    ref, _ = oracle.run_batch(b)
+    U.compare(U.prefill(U.Dev(b)), ref, "bf16", "many_short/prefill")
+    L = rng.integers(1, 200, size=517)
+    b = _mk(92, L, np.ones_like(L), Hq=48, Hkv=8, D=128, W=0)
+    ref, _ = oracle.run_batch(b)
+    d = U.Dev(b)
+    for s in (1, 2, 0):
+        _say(f"many short sequences: decode, 517 sequences, splits={s}")
+        U.compare(U.decode(d, splits=s), ref, "bf16", f"many_short/decode/s{s}")
