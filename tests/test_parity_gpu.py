@@ -595,3 +595,19 @@ def test_many_short_sequences():
     for s in (1, 2, 0):
         _say(f"many short sequences: decode, 517 sequences, splits={s}")
         U.compare(U.decode(d, splits=s), ref, "bf16", f"many_short/decode/s{s}")
+
+
+def test_full_block_table():
+    """Sequences that use every entry of their block-table row (L = 16 x
+    max_blocks_per_seq), next to ones a page and a key short of it."""
+    for kind, n in (("prefill", [1024, 1008, 1023]), ("decode", [1, 1, 1])):
+        b = _mk(95, [1024, 1008, 1023], n, Hq=24, Hkv=8, D=128, W=0, max_blocks=64)
+        assert b.block_table.shape[1] == 64 and (b.block_table[0] >= 0).all()
+        ref, _ = oracle.run_batch(b)
+        d = U.Dev(b)
+        _say(f"full block table: {kind}")
+        if kind == "prefill":
+            U.compare(U.prefill(d), ref, "bf16", "full_table/prefill")
+        else:
+            for s in (1, 4):
+                U.compare(U.decode(d, splits=s), ref, "bf16", f"full_table/decode/s{s}")
