@@ -77,6 +77,12 @@ PREFILL_CASES = [
     # the KV head counts 16 local / 8 global are a reading, not on the pages).
     ("small_local", 18, [1100, 300], [1100, 300], 32, 16, 128, 512, 512, "bf16"),
     ("small_global", 19, [900, 2000], [900, 400], 32, 8, 128, 0, 8192, "bf16"),
+    # Group sizes that leave columns of a 128-column block unused and split
+    # a token's heads across waves (bq = 25, 18, 10), and a distance clamp
+    # inside the window (R = 200 < W = 300).
+    ("g5_clamp_in_window", 23, [700, 260], [700, 130], 40, 8, 128, 300, 200, "bf16"),
+    ("g7_global", 24, [600, 90], [600, 90], 28, 4, 128, 0, 8192, "bf16"),
+    ("g12_local", 25, [500, 41], [500, 41], 48, 4, 128, 512, 512, "bf16"),
 ]
 
 
@@ -215,6 +221,10 @@ DECODE_CASES = [
     # The smaller model's shapes (32 query heads; KV heads 16 / 8, a reading).
     ("small_local", 49, [1500, 513, 17], 32, 16, 128, 512, 512, [1, 2, 0]),
     ("small_global", 51, [5000, 4096, 33], 32, 8, 128, 0, 8192, [1, 8, 0]),
+    # Group sizes 5, 7 and 12, and a distance clamp inside the window.
+    ("g5_clamp_in_window", 52, [700, 299, 301, 30], 40, 8, 128, 300, 200, [1, 3, 0]),
+    ("g7_global", 53, [2000, 17], 28, 4, 128, 0, 8192, [1, 4]),
+    ("g12_local", 54, [1300, 512], 48, 4, 128, 512, 512, [1, 2]),
 ]
 
 
