@@ -144,8 +144,14 @@ decode_kernel(const DecodeParams P) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = NH > 1 ? __builtin_amdgcn_readfirstlane(tid >> 6) : 0;
+  // Workgroup (x, y, z) runs on XCD (x + gridDim.x (y + gridDim.y z)) mod 8.
+  // With y the split itself, an XCD would get one parity of split index for
+  // every sequence, and the first splits are the ones that are always full;
+  // rotating the split by the sequence spreads full and partial splits over
+  // the XCDs.
   const int g0 = blockIdx.x * NH, g = g0 + wave;
-  const int split = blockIdx.y, b = blockIdx.z;
+  const int b = blockIdx.z;
+  const int split = (int)((blockIdx.y + blockIdx.z) % gridDim.y);
   const int col = lane & 15, u4 = lane >> 4;
   const int G = P.group, R = P.rel_len, W = P.window;
   const bool cval = col < G;
