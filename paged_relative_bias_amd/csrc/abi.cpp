@@ -234,7 +234,8 @@ inkling_status_t prefill_impl(const void* q, const void* k_new, const void* v_ne
   if ((int64_t)16 * dims->num_kv_heads * dims->head_dim * (int64_t)esz >= (1LL << 31) ||
       (int64_t)p.bq * dims->num_q_heads * dims->rel_len * (int64_t)esz >= (1LL << 31))
     return INKLING_ERR_UNSUPPORTED;
-  if ((int64_t)p.nqb * dims->num_seqs * dims->num_kv_heads >= (1LL << 31))
+  if ((int64_t)p.nqb * dims->num_seqs * dims->num_kv_heads >= (1LL << 31) ||
+      ((int64_t)dims->total_q / p.bq + dims->num_seqs) * dims->num_kv_heads >= (1LL << 31))
     return INKLING_ERR_UNSUPPORTED;
   const hipError_t e = bf16_fast ? launch_prefill_bf16(p, static_cast<hipStream_t>(stream))
                                  : launch_prefill(p, dims->dtype, dims->head_dim,

@@ -9,9 +9,11 @@
 //
 // Work decomposition and columns are those of the generic prefill kernel:
 // one workgroup per (block of bq query tokens, sequence b, KV head g) on an
-// XCD-remapped 1-D grid; the 4 waves' 128 MFMA columns are (query head in
-// group, token) pairs, token-major, 32 per wave.  Key tiles of 32 keys sweep
-// the union of the block's visible ranges through two LDS stages; per wave
+// XCD-remapped 1-D grid, here sized from the batch's total query tokens
+// rather than sequences x the longest; the 4 waves' 128 MFMA columns are
+// (query head in group, token) pairs, token-major, 32 per wave.  Key tiles
+// of 32 keys sweep the union of the block's visible ranges through two LDS
+// stages; per wave
 // and tile S^T = K . Q^T (32x32x16 bf16 MFMA), x = scale * S + bias, a
 // softmax against a per-column reference (the column's max in its first
 // tile with a visible key, raised, with the accumulators rescaled in
@@ -115,20 +117,56 @@ prefill_bf16_kernel(const PrefillParams P) {
   const uint32_t wlim = W > 0 ? (uint32_t)W : 0x80000000u;
   const int64_t hq = P.hq;
 
-  // XCD-aware work index: workgroup id x runs on XCD x % 8; give each XCD
-  // a contiguous range of work (query block fastest, heaviest first).
-  const int total = P.nqb * P.num_seqs * P.hkv;
+  // Work list.  Sequence b owns the block indices [S(b), S(b + 1)) with
+  // S(b) = floor(cu_q_lens[b] / bq) + b: at least its ceil(n_b / bq) query
+  // blocks and at most one more, NB = S(B) in all, so a batch of short rows
+  // beside long chunks launches no workgroup per (row, unused block).  A
+  // sequence's blocks run last (heaviest) first.  XCD-aware: workgroup id x
+  // runs on XCD x % 8, and each XCD gets a contiguous range of the work, so
+  // neighbouring query blocks of one (sequence, KV head) share its L2.
+  const int Bn = P.num_seqs;
+  const int NB = P.total_q / bq + Bn;
+  const int total = NB * P.hkv;
   const int per_xcd = (total + 7) >> 3;
   const int w = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
   if (w >= total) return;
-  const int qb = P.nqb - 1 - w % P.nqb;
-  const int bg = w / P.nqb;
-  const int b = bg % P.num_seqs, g = bg / P.num_seqs;
+  const int j = w % NB, g = w / NB;
+  // The sequence is the largest b with S(b) <= j (S increases with b).  Each
+  // wave finds it on its own, from 64 candidates per round; metadata that
+  // is not monotone still yields some b in [0, B).
+  int b = 0, cq0 = 0, cq1 = 0, Lraw = 0;
+  if (Bn <= 63) {
+    // One round trip: lanes 0..B hold cu_q_lens, lanes 0..B-1 seq_lens.
+    const int i = imin(lane, Bn);
+    const int cq = iclamp(P.cu_q_lens[i], 0, P.total_q);
+    const int sl = P.seq_lens[imin(lane, Bn - 1)];
+    const uint64_t m = __builtin_amdgcn_ballot_w64(lane < Bn && cq / bq + lane <= j);
+    b = imax(__builtin_popcountll(m) - 1, 0);
+    cq0 = __builtin_amdgcn_readlane(cq, b);
+    cq1 = __builtin_amdgcn_readlane(cq, b + 1);
+    Lraw = __builtin_amdgcn_readlane(sl, b);
+  } else {
+    int span = Bn;                                       // b is in [b, b + span)
+    while (span > 1) {                                   // wave-uniform
+      const int step = (span + 63) / 64;
+      const int idx = b + lane * step;
+      const int S = lane * step < span ? iclamp(P.cu_q_lens[idx], 0, P.total_q) / bq + idx
+                                       : 0x7fffffff;
+      const uint64_t m = __builtin_amdgcn_ballot_w64(S <= j);
+      b += imax(__builtin_popcountll(m) - 1, 0) * step;
+      span = imin(step, Bn - b);
+    }
+    cq0 = iclamp(P.cu_q_lens[b], 0, P.total_q);
+    cq1 = iclamp(P.cu_q_lens[b + 1], 0, P.total_q);
+    Lraw = P.seq_lens[b];
+  }
+  const int qb = (cq1 / bq + b + 1) - 1 - j;             // S(b + 1) - 1 - j
+  if (qb < 0) return;
 
   // Sequence metadata, clamped so that no read leaves the arguments.
-  const int q0 = iclamp(P.cu_q_lens[b], 0, P.total_q);
-  const int q1 = iclamp(P.cu_q_lens[b + 1], q0, P.total_q);
-  const int L = iclamp(P.seq_lens[b], 0, P.max_blocks * 16);
+  const int q0 = cq0;
+  const int q1 = imax(cq1, q0);
+  const int L = iclamp(Lraw, 0, P.max_blocks * 16);
   const int n = imin(q1 - q0, L);
   const int t0 = qb * bq;
   if (t0 >= n) return;
@@ -622,7 +660,7 @@ hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) {
                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   });
   if (attr != hipSuccess) return attr;
-  const int64_t total = (int64_t)p.nqb * p.num_seqs * p.hkv;
+  const int64_t total = (int64_t)(p.total_q / p.bq + p.num_seqs) * p.hkv;
   const int64_t grid = ((total + 7) / 8) * 8;
   if (p.k_new != nullptr)
     prefill_bf16_kernel<true><<<dim3((unsigned)grid), dim3(kPrefillWaves * 64),
