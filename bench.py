@@ -18,8 +18,11 @@ serving configuration (global decode at the library's split count and at 1,
 mixed batch as one call and split; long-context global decode; and the
 smaller model's shapes).
 
-Timing: W untimed warm-up steps, then exactly K steps bracketed by
-torch.cuda.synchronize(); two HIP events on the launch stream around the
+Timing: a settle phase of back-to-back steps covering at least
+--settle-ms of GPU time (the clocks and the memory system reach their
+steady state only after tens of ms of sustained work: local decode runs
+3-4% slower over its first few ms), then W untimed warm-up steps, then
+exactly K steps bracketed by torch.cuda.synchronize(); two HIP events on the launch stream around the
 timed region give the back-to-back mean launch time, from which the
 roofline fractions are computed, and a separate pass with an event pair
 around every step (at least 50) gives the median and p10/p90 launch
@@ -298,10 +301,26 @@ class Workload:
             if st != 0:
                 raise binding.InklingError(st, "step")
 
-    def time(self, steps, warmup):
+    def time(self, steps, warmup, settle_ms=0.0):
         import torch
+        # Settle: a short probe estimates the step time, then enough
+        # back-to-back steps to cover settle_ms of GPU time, with no
+        # synchronisation between them.
+        n0 = 0
+        if settle_ms > 0:
+            for i in range(4):
+                self.step(i)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(8):
+                self.step(i)
+            torch.cuda.synchronize()
+            est_ms = max((time.perf_counter() - t0) * 1e3 / 8, 1e-3)
+            n0 = int(min(20000, math.ceil(settle_ms / est_ms)))
+            for i in range(n0):
+                self.step(i)
         for i in range(warmup):
-            self.step(i)
+            self.step(n0 + i)
         torch.cuda.synchronize()
         # Timed region: K back-to-back steps, HIP events on the launch stream
         # at its two ends only (an event between launches adds its own gap).
@@ -391,8 +410,9 @@ def run_record(record_name, batch, splits, args, dev, steps, warmup, cpu, graph=
     kind = "global_mixed_split" if record_name == "global_mixed_split" else batch.name
     wl = Workload(kind, batch, splits=splits, append=args.append, graph=graph,
                   replicas=args.replicas, dev=dev)
-    t = wl.time(steps, warmup)
+    t = wl.time(steps, warmup, args.settle_ms)
     rec = record_for(kind, batch, wl, t, record_name, cpu)
+    rec["config"]["settle_ms"] = args.settle_ms
     rec["config"]["seed"] = args.seed
     rec["config"]["launch"] = "hip_graph" if graph else "eager"
     rec["config"]["append"] = bool(args.append)
@@ -427,6 +447,8 @@ def main():
     # Prefill launches (~0.7 ms) need about 20 ms of back-to-back work before
     # their duration settles; 50 untimed steps cover that for every workload.
     ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--settle-ms", type=float, default=50.0,
+                    help="back-to-back steps covering this much GPU time before the warm-up steps")
     ap.add_argument("--workload", default=None, choices=WORKLOAD_CHOICES,
                     help="time only this workload (default: the headline and every other)")
     ap.add_argument("--headline-only", action="store_true",
