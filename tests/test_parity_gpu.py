@@ -621,3 +621,20 @@ def test_full_block_table():
         else:
             for s in (1, 4):
                 U.compare(U.decode(d, splits=s), ref, "bf16", f"full_table/decode/s{s}")
+
+
+@pytest.mark.parametrize("nseq", [63, 64, 130])
+def test_prefill_work_list(nseq):
+    """Batches at and past the one-round sequence search (63 sequences) with
+    multi-block sequences beside one-token rows and empty ones, on a local
+    and a global layer: every query block of every sequence is computed
+    once, in any position of the work list."""
+    rng = np.random.default_rng(100 + nseq)
+    n = rng.integers(0, 160, size=nseq)
+    n[rng.random(nseq) < 0.3] = 1
+    L = n + rng.integers(0, 300, size=nseq)
+    for W in (512, 0):
+        _say(f"prefill work list: {nseq} sequences, W={W}")
+        b = _mk(110 + nseq + W, L, n, Hq=48, Hkv=16 if W else 8, D=128, W=W)
+        ref, _ = oracle.run_batch(b)
+        U.compare(U.prefill(U.Dev(b)), ref, "bf16", f"work_list/{nseq}/W{W}")
