@@ -247,10 +247,15 @@ prefill_bf16_kernel(const PrefillParams P) {
   // [w0, w0 + 40) of its row with w0 = floor_to(p - 31, 8) - kt (kt is a
   // multiple of 16), which holds distances p - kt - 31 .. p - kt.  LDS load
   // m of a wave writes chunks 64 m .. 64 m + 63 of its region: chunk c is
-  // part c % 5 of column c / 5's window.  Chunks before or past the buffer
-  // read zero (their distances are masked); chunks of padding columns, and
-  // of the last load's upper half, read nothing.
+  // part c % 5 of column c / 5's window.  A chunk's entry lies on a multiple
+  // of 8, and R is one: a chunk before its row's start or past its end holds
+  // only masked distances (future keys, or distances >= R on a window tile),
+  // so it reads the row's first or last chunk instead; reading it from the
+  // neighbouring row would fetch that row's line a whole sweep before the
+  // row's own column reaches it.  Chunks of padding columns, and of the last
+  // load's upper half, read nothing.
   uint32_t b_dma[3];
+  int b_pos[3];
 #pragma unroll
   for (int m = 0; m < 3; ++m) {
     const int c = 64 * m + lane;
@@ -259,9 +264,9 @@ prefill_bf16_kernel(const PrefillParams P) {
     const int rh = rc % G, rt = t0 + rc / G;
     const bool ok = bc < 32 && rh < G && rt < tend;
     const int w0 = floor_to(pbase + rt - (kN - 1), 8);
-    b_dma[m] = ok ? (uint32_t)((rt - t0) * (int)hq + g * G + rh) * (uint32_t)R * SZ +
-                        (uint32_t)(w0 + 8 * part) * SZ
-                  : 0xfffffff0u;
+    b_dma[m] = ok ? (uint32_t)((rt - t0) * (int)hq + g * G + rh) * (uint32_t)R * SZ
+                  : 0xf0000000u;      // past any bias buffer: reads zero
+    b_pos[m] = w0 + 8 * part;
   }
   // The lane's 16 elements: entries D0 - 15 .. D0 of the window, i.e. 32
   // bytes from entry ((pc - 31) & 7) + 16 (1 - u) of its column's window.
@@ -355,8 +360,8 @@ prefill_bf16_kernel(const PrefillParams P) {
     const uint32_t bl = sgpr_u32(kBiasOff + (uint32_t)(bs * kPrefillWaves + wave) * kBiasWave);
 #pragma unroll
     for (int m = 0; m < 3; ++m) {
-      // Below zero the offset wraps to a large value and reads zero.
-      const uint32_t off = b_dma[m] - (uint32_t)kt * SZ;
+      const int pos = imin(imax(b_pos[m] - kt, 0), R - 8);
+      const uint32_t off = b_dma[m] + (uint32_t)pos * SZ;
       const uint32_t ml = sgpr_u32(bl + 1024u * (uint32_t)m);
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
