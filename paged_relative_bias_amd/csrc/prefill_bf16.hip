@@ -175,16 +175,22 @@ prefill_bf16_kernel(const PrefillParams P) {
   const int jb = W > 0 ? imax(0, pbase + t0 - W + 1) : 0;   // block's first key
   const int je = pbase + tend;                              // one past last key
 
+  // A block whose columns all fit one wave (G x tokens <= 32: single-token
+  // rows of a mixed batch, a sequence's last few tokens) gives every wave
+  // those columns and a quarter of the key tiles instead (tile i to wave
+  // i mod 4); the waves' partial results are merged at the end.
+  const bool ksplit = G * (tend - t0) <= 32;              // workgroup-uniform
+  const int wsel = ksplit ? 0 : wave;
   // This lane's column (query head, token) and lane half.
   const int col = lane & 31, u = lane >> 5;
-  const int wc = wave * 32 + col;
+  const int wc = wsel * 32 + col;
   const int hh = wc % G;
   const int tc = t0 + wc / G;
   const bool cval = hh < G && tc < tend;
   const int h = g * G + (hh < G ? hh : 0);
   const int pc = pbase + tc;
   // The wave's token range and its visible key range.
-  const int c_lo = wave * 32, c_hi = imin(c_lo + 31, G * bq - 1);
+  const int c_lo = wsel * 32, c_hi = imin(c_lo + 31, G * bq - 1);
   const int wt_lo = t0 + c_lo / G;
   const int wt_hi = imin(t0 + c_hi / G + 1, tend);   // exclusive
   const bool wact = c_lo < G * bq && wt_lo < tend;
@@ -260,7 +266,7 @@ prefill_bf16_kernel(const PrefillParams P) {
   for (int m = 0; m < 3; ++m) {
     const int c = 64 * m + lane;
     const int bc = c / kWinChunks, part = c - bc * kWinChunks;
-    const int rc = wave * 32 + bc;
+    const int rc = wsel * 32 + bc;
     const int rh = rc % G, rt = t0 + rc / G;
     const bool ok = bc < 32 && rh < G && rt < tend;
     const int w0 = floor_to(pbase + rt - (kN - 1), 8);
@@ -288,7 +294,10 @@ prefill_bf16_kernel(const PrefillParams P) {
   const int vis_cap = W > 0 ? W - 1 : 0x7fffffff;
   auto unclamped = [&](int kt) { return imin((wje - 1) - kt, vis_cap) <= R - 1; };
   auto all_clamped = [&](int kt) { return (pbase + wt_lo) - (kt + kN - 1) >= R - 1; };
-  auto wave_tile = [&](int kt) { return wact && kt < wje && kt + kN > wjb; };
+  const int kt_first = jb & ~15;
+  auto wave_tile = [&](int kt) {
+    return wact && kt < wje && kt + kN > wjb && (!ksplit || ((kt - kt_first) >> 5) % kPrefillWaves == wave);
+  };
 
   // K/V of the tile at kt into LDS stage st.  The descriptors of the tile's
   // two pages end at key je (keys past it, and whole tiles past the last,
@@ -632,6 +641,47 @@ prefill_bf16_kernel(const PrefillParams P) {
   // Prefetches past the last tile may be outstanding: drain them before the
   // wave ends.
   __builtin_amdgcn_s_waitcnt(0);
+
+  if (ksplit) {
+    // Waves 1..3 hand their accumulators, row sums and references to wave 0
+    // through LDS (every wave's loads have landed and its reads are done),
+    // which merges them by log-sum-exp weights.
+    lds_barrier();
+    float* xs = reinterpret_cast<float*>(smem);
+    constexpr int kXs = 66 * 64;                          // floats per wave
+    if (wave > 0) {
+      float* d = xs + (wave - 1) * kXs + lane;
+#pragma unroll
+      for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) d[(16 * dt + i) * 64] = acc[dt][i];
+      d[64 * 64] = m_ref;
+      d[65 * 64] = l_run;
+    }
+    lds_barrier();
+    if (wave > 0) return;
+    float mw[kPrefillWaves - 1];
+    float M = m_ref;
+#pragma unroll
+    for (int w = 0; w < kPrefillWaves - 1; ++w) {
+      mw[w] = xs[w * kXs + 64 * 64 + lane];
+      M = fmaxf(M, mw[w]);
+    }
+    const float e0 = m_ref == kNegInf ? 0.f : fast_exp2((m_ref - M) * kLog2e);
+#pragma unroll
+    for (int dt = 0; dt < kD / 32; ++dt) acc[dt] *= e0;
+    l_run *= e0;
+#pragma unroll
+    for (int w = 0; w < kPrefillWaves - 1; ++w) {
+      const float e = mw[w] == kNegInf ? 0.f : fast_exp2((mw[w] - M) * kLog2e);
+      const float* src = xs + w * kXs + lane;
+#pragma unroll
+      for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[dt][i] += e * src[(16 * dt + i) * 64];
+      l_run += e * src[65 * 64];
+    }
+  }
 
   if (!wact) return;
   const float lt = l_run + xor_lane(l_run, 32);
