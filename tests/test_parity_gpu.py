@@ -83,6 +83,11 @@ PREFILL_CASES = [
     ("g5_clamp_in_window", 23, [700, 260], [700, 130], 40, 8, 128, 300, 200, "bf16"),
     ("g7_global", 24, [600, 90], [600, 90], 28, 4, 128, 0, 8192, "bf16"),
     ("g12_local", 25, [500, 41], [500, 41], 48, 4, 128, 512, 512, "bf16"),
+    # Blocks of at most 32 columns, whose key tiles the four waves share:
+    # one- and two-token blocks that see only their own key (W = 1), and an
+    # exactly full 32-column block (G = 1) over 62 key tiles.
+    ("ksplit_window_1", 26, [85, 300], [85, 2], 12, 4, 128, 1, 8, "bf16"),
+    ("ksplit_g1_32_cols", 27, [600, 2000], [600, 32], 4, 4, 128, 0, 8192, "bf16"),
 ]
 
 
