@@ -474,8 +474,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(attention shards by head with no exchange; see the design notes). "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(attention shards by KV head with no exchange between GPUs). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
