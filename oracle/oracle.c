@@ -32,8 +32,8 @@
  *   out[i][h][:] = sum over visible exp(s_j - M) / Z * V_j
  *   lse[i][h]    = M + ln Z
  *
- * Readings where the pages are silent (each is listed with its reason in the
- * design notes): the window holds W keys including the query itself (d < W);
+ * Readings where the pages are silent: the window holds W keys including the
+ * query itself (d < W);
  * the distance index is clamped to R - 1; query position is bottom-right
  * aligned (p = L_b - n_b + t); query head h uses KV head h / (Hq / Hkv); an
  * empty visible set gives out = 0 and lse = -inf.
