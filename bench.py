@@ -72,12 +72,14 @@ SECONDARY = [
     ("local_prefill", [("local_prefill", 0)]),
     ("global_mixed", [("global_mixed", 0), ("global_mixed_split", 0)]),
     ("long_global_decode", [("long_global_decode", 0)]),
+    ("long_global_prefill", [("long_global_prefill", 0)]),
     ("small_local_decode", [("small_local_decode", 0)]),
     ("small_global_decode", [("small_global_decode", 0)]),
     ("small_local_prefill", [("small_local_prefill", 0)]),
 ]
 WORKLOAD_CHOICES = ["local_decode", "global_decode", "local_prefill", "global_mixed",
                     "global_mixed_split", "tiny_prefill", "long_global_decode",
+                    "long_global_prefill",
                     "small_local_decode", "small_global_decode", "small_local_prefill"]
 
 

@@ -226,7 +226,7 @@ inkling_status_t prefill_impl(const void* q, const void* k_new, const void* v_ne
   // bf16 with head_dim 128 runs the specialised kernel (with or without the
   // fused append).
   const bool bf16_fast = dims->dtype == INKLING_DTYPE_BF16 && dims->head_dim == 128;
-  if ((bf16_fast ? prefill_bf16_lds_bytes(p.pid_cap)
+  if ((bf16_fast ? prefill_bf16_lds_bytes()
                  : prefill_lds_bytes(dims->dtype, dims->head_dim, waves, p.sb_pitch, p.pid_cap)) >
       160 * 1024)
     return INKLING_ERR_UNSUPPORTED;

@@ -78,7 +78,7 @@ hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_dim, hipSt
 size_t prefill_lds_bytes(int dtype, int head_dim, int waves, int sb_pitch, int pid_cap);
 // The bf16, head_dim 128 prefill without append (the serving shapes).
 hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream);
-size_t prefill_bf16_lds_bytes(int pid_cap);
+size_t prefill_bf16_lds_bytes();
 hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim,
                          hipStream_t stream);
 size_t decode_lds_bytes(const DecodeParams& p, int dtype, int head_dim);

@@ -78,7 +78,7 @@ constexpr int kWinChunks = 5;
 constexpr uint32_t kBiasWave = 3 * 1024;     // bytes per wave and bias stage
 constexpr int kBiasStages = 3;
 constexpr uint32_t kBiasOff = 2 * kStage;
-constexpr uint32_t kPidOff = kBiasOff + (uint32_t)kBiasStages * kPrefillWaves * kBiasWave;
+constexpr uint32_t kLdsBytes = kBiasOff + (uint32_t)kBiasStages * kPrefillWaves * kBiasWave;
 
 // Waits until at most N of this wave's vector-memory loads are in flight
 // (the other counters are left alone).
@@ -197,20 +197,13 @@ prefill_bf16_kernel(const PrefillParams P) {
   const int wjb = W > 0 ? imax(0, pbase + wt_lo - W + 1) : 0;
   const int wje = pbase + wt_hi;
 
-  // LDS: two stages of (K tile, V tile), three stages of the waves' bias
-  // windows, the page-id table.
-  int* pid_lds = reinterpret_cast<int*>(smem + kPidOff);
-
-  // Page ids of keys [jb, je).
-  const int pg_lo = jb >> 4;
-  const int npg = imin(((je - 1) >> 4) - pg_lo + 1, P.pid_cap);
-  {
-    const int seq_pages = (L + 15) >> 4;
-    const __amdgpu_buffer_rsrc_t bt_rsrc =
-        make_rsrc(P.block_table + (int64_t)b * P.max_blocks, (uint32_t)seq_pages * 4u);
-    for (int i = tid; i < npg; i += blockDim.x)
-      pid_lds[i] = iclamp((int)bload32(bt_rsrc, (uint32_t)(pg_lo + i) * 4u), 0, P.num_blocks - 1);
-  }
+  // LDS: two stages of (K tile, V tile) and three stages of the waves' bias
+  // windows.  Page ids are read with scalar loads a tile ahead of their use,
+  // so LDS does not grow with the context.  The sequence's block-table row
+  // is read-only for the kernel's lifetime (constant address space).
+  using const_i32 = const __attribute__((address_space(4))) int;
+  const_i32* bt_row = (const_i32*)(P.block_table + (int64_t)b * P.max_blocks);
+  const int last_page = imax(((L + 15) >> 4) - 1, 0);
 
   // Q^T operand (B of the QK MFMA), held for the whole kernel.
   bf16x8 qop[8];
@@ -302,11 +295,13 @@ prefill_bf16_kernel(const PrefillParams P) {
   // K/V of the tile at kt into LDS stage st.  The descriptors of the tile's
   // two pages end at key je (keys past it, and whole tiles past the last,
   // read zero without traffic).  No control flow around any load.
-  // The tile's two page ids (read from the LDS table ahead of their use).
+  // The tile's two page ids.  Pages past the sequence's last read its last
+  // page (such tiles' descriptors are empty), and every id is clamped into
+  // the pool.
   auto page_ids = [&](int kt) {
-    const int pi0 = imin((kt >> 4) - pg_lo, P.pid_cap - 1);        // >= 0
-    const int pi1 = imin(pi0 + 1, P.pid_cap - 1);
-    return make_int2(pid_lds[pi0], pid_lds[pi1]);
+    const int p0 = imin(kt >> 4, last_page), p1 = imin((kt >> 4) + 1, last_page);
+    return make_int2(iclamp(bt_row[p0], 0, P.num_blocks - 1),
+                     iclamp(bt_row[p1], 0, P.num_blocks - 1));
   };
   auto issue_kv = [&](int kt, int st, int2 pids) {
     const uint64_t page0 = (uint32_t)__builtin_amdgcn_readfirstlane(pids.x);
@@ -398,10 +393,8 @@ prefill_bf16_kernel(const PrefillParams P) {
   // `between` issues the loads of later tiles: it runs after this tile's
   // LDS reads are issued and before their first use, so that its scalar
   // work overlaps their latency.
-  auto compute = [&](int kt, int st, int bs, auto&& between) {
-    // The next tile's page ids first: their LDS reads complete in order, so
-    // the wait for them in `between` does not wait for this tile's operands.
-    const int2 pids = page_ids(kt + kN);
+  // pids are the next tile's page ids, loaded one step earlier.
+  auto compute = [&](int kt, int st, int bs, int2 pids, auto&& between) {
     if (!wave_tile(kt)) {                                 // wave-uniform
       between(pids);
       return;
@@ -583,20 +576,17 @@ prefill_bf16_kernel(const PrefillParams P) {
   // wave's bias region is its own).  Loads past the last tile read nothing,
   // so no load sits under control flow.  Nothing the compiler sees is loaded
   // in the loop outside the rare clamp path, so it adds no waits of its own.
-  lds_barrier();                                         // page ids ready
   if constexpr (APPEND) {
     // Store this workgroup's tokens' new K/V rows of head g into the cache
-    // (16 chunks of 16 bytes per row and tensor).  With valid metadata every
-    // new key's page is in the table; a clipped table only follows from
-    // lengths above max_seq_len, whose result is unspecified: skip those.
+    // (16 chunks of 16 bytes per row and tensor).  Every new key lies below
+    // L, so its page is in the sequence's block-table row.
     const int chunks = (tend - t0) * 32;
     for (int c = tid; c < chunks; c += blockDim.x) {
       const int t = t0 + (c >> 5), r = c & 31;
       const bool isv = r >= 16;
       const int key = pbase + t;
-      const int pi = (key >> 4) - pg_lo;
-      if (pi >= npg) continue;
-      const uint64_t page = (uint32_t)pid_lds[pi];
+      const uint64_t page = (uint32_t)iclamp(
+          P.block_table[(int64_t)b * P.max_blocks + imin(key >> 4, last_page)], 0, P.num_blocks - 1);
       const uint64_t dst = page * page_bytes + (uint64_t)(key & 15) * slot_bytes + head_bytes +
                            (uint64_t)(r & 15) * 16u;
       const uint64_t src = (uint64_t)(q0 + t) * slot_bytes + head_bytes + (uint64_t)(r & 15) * 16u;
@@ -624,15 +614,23 @@ prefill_bf16_kernel(const PrefillParams P) {
           make_uint4(0u, 0u, 0u, 0u);
     }
   }
+  // Page ids are loaded a step ahead and completed before the step's
+  // barrier (the empty asm reads them there), so that no wait for them
+  // falls between a tile's LDS reads and their use.
+  int2 pids_next = page_ids(kt + kN);
+  asm volatile("" ::"s"(pids_next.x), "s"(pids_next.y));
   lds_barrier();
   while (true) {
-    compute(kt, st, bs, [&](int2 pids) {
-      issue_kv(kt + kN, st ^ 1, pids);
+    const int2 pids = pids_next;
+    pids_next = page_ids(kt + 2 * kN);
+    compute(kt, st, bs, pids, [&](int2 p) {
+      issue_kv(kt + kN, st ^ 1, p);
       issue_bias(kt + 2 * kN, bs == 0 ? 2 : bs - 1);
     });
     if (kt + kN >= je) break;                            // workgroup-uniform
     wait_vmem<3>();
     if constexpr (APPEND) patch_new(kt + kN, st ^ 1);
+    asm volatile("" ::"s"(pids_next.x), "s"(pids_next.y));
     lds_barrier();
     kt += kN;
     st ^= 1;
@@ -701,7 +699,7 @@ prefill_bf16_kernel(const PrefillParams P) {
 
 }  // namespace
 
-size_t prefill_bf16_lds_bytes(int pid_cap) { return (size_t)kPidOff + (size_t)pid_cap * 4; }
+size_t prefill_bf16_lds_bytes() { return (size_t)kLdsBytes; }
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) {
   // Raise the kernel's dynamic LDS limit once per process (thread-safe).
@@ -719,10 +717,10 @@ hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t stream) {
   const int64_t grid = ((total + 7) / 8) * 8;
   if (p.k_new != nullptr)
     prefill_bf16_kernel<true><<<dim3((unsigned)grid), dim3(kPrefillWaves * 64),
-                                prefill_bf16_lds_bytes(p.pid_cap), stream>>>(p);
+                                prefill_bf16_lds_bytes(), stream>>>(p);
   else
     prefill_bf16_kernel<false><<<dim3((unsigned)grid), dim3(kPrefillWaves * 64),
-                                 prefill_bf16_lds_bytes(p.pid_cap), stream>>>(p);
+                                 prefill_bf16_lds_bytes(), stream>>>(p);
   return hipGetLastError();
 }
 

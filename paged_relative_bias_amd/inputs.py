@@ -288,6 +288,21 @@ def long_global_decode(seed: int = 0, batch: int = 4, lo: int = 32768,
                       poison=poison, name="long_global_decode")
 
 
+def long_global_prefill(seed: int = 0, batch: int = 2, chunk: int = 1024,
+                        lo: int = 32768, hi: int = 98304, poison: bool = True) -> Batch:
+    """Chunked prefill at long context on a global layer: 2 chunks of 1024 new
+    tokens on U[32768, 98304] cached tokens; Hq=48, Hkv=8, full causal,
+    R=8192 (distances past 8191 read the last entry)."""
+    rng = np.random.default_rng(seed)
+    cached = rng.integers(lo, hi + 1, size=batch)
+    L = cached + chunk
+    return make_batch(rng, L, np.full(batch, chunk, dtype=np.int64), num_q_heads=HQ,
+                      num_kv_heads=HKV_GLOBAL, head_dim=HEAD_DIM, window=0,
+                      rel_len=MAX_CONTEXT,
+                      max_blocks_per_seq=(hi + chunk + BLOCK_SIZE - 1) // BLOCK_SIZE,
+                      poison=poison, name="long_global_prefill")
+
+
 # The smaller model of the same family (TensorRT-LLM Inkling page, commit
 # list: the Inkling-Small accuracy commit gives 42 layers and hidden size
 # 4096, and no head counts).  Reading: head_dim stays 128, so 32 query heads,
@@ -334,6 +349,7 @@ WORKLOADS = {
     "local_prefill": local_prefill,
     "global_mixed": global_mixed,
     "long_global_decode": long_global_decode,
+    "long_global_prefill": long_global_prefill,
     "small_local_decode": small_local_decode,
     "small_global_decode": small_global_decode,
     "small_local_prefill": small_local_prefill,

@@ -88,6 +88,9 @@ PREFILL_CASES = [
     # exactly full 32-column block (G = 1) over 62 key tiles.
     ("ksplit_window_1", 26, [85, 300], [85, 2], 12, 4, 128, 1, 8, "bf16"),
     ("ksplit_g1_32_cols", 27, [600, 2000], [600, 32], 4, 4, 128, 0, 8192, "bf16"),
+    # Chunks at long context on a global layer: page ids over 2,500 pages per
+    # sequence, the distance clamp active (R = 8192), short last blocks.
+    ("long_context_global", 28, [40000, 33000], [24, 5], 48, 8, 128, 0, 8192, "bf16"),
 ]
 
 
