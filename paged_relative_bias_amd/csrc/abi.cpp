@@ -220,7 +220,8 @@ inkling_status_t prefill_impl(const void* q, const void* k_new, const void* v_ne
   p.sb_pitch = row_dw * 4;
   p.nqb = (dims->max_q_len + p.bq - 1) / p.bq;
   p.num_seqs = dims->num_seqs;
-  // Pages a workgroup's key range can touch.
+  // Pages a workgroup's key range can touch (the generic kernel's LDS page
+  // table; the bf16 kernel reads page ids with scalar loads instead).
   const int64_t span = window > 0 ? (int64_t)p.bq + window - 1 : (int64_t)dims->max_seq_len;
   p.pid_cap = (int32_t)std::min<int64_t>(dims->max_blocks_per_seq, (span + 15) / 16 + 2);
   // bf16 with head_dim 128 runs the specialised kernel (with or without the
